@@ -1,0 +1,136 @@
+"""fp64 CPU oracle for the DDTS recurrence of Rodimus (TEST INFRASTRUCTURE).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package.  The product path (the HIP library and its Python binding)
+never imports it, and it imports nothing from the product path.
+
+``fwd`` and ``decode`` wrap the C implementation in ``ddts_oracle.c``: the
+plain token-by-token recurrence
+
+    alpha_t = exp(-g_t * tau_t),  alpha_hat_t = g_t ** tau_t      (over dk)
+    S_t = diag(alpha_t) S_{t-1} + (alpha_hat_t * k_t)(beta_hat_t * v_t)^T
+    o_t = S_t^T q_t
+
+in float64.  The gate formulas follow the Rodimus* digest page
+(digest.lyk-ai.com), section "Method"; the placement of alpha and alpha_hat on
+the dk rows follows the authors' rebuttal page (paperhub.cn), the
+"Efficient Parallelization" bullet (selection only along n).
+
+Every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` against a brute-force quadratic form, library
+matmuls in the special cases tau = 0 and constant gates, a division-based
+closed form for dk = dv = 1, the g = 0 invariant, linearity and bitwise
+carry-over.
+
+Inputs may be any numpy floating dtype (bf16 inputs arrive as their exact
+float32 upcast); they are converted to float64 exactly before the C call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ddts_oracle.c")
+_LIB = os.path.join(_HERE, "libddts_oracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-pthread"]
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (IEEE, no fast-math).  Returns the .so path."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.ddts_oracle_fwd.restype = ctypes.c_int
+        lib.ddts_oracle_fwd.argtypes = [ctypes.c_int] * 5 + [dp] * 9 + [ctypes.c_int]
+        lib.ddts_oracle_decode.restype = ctypes.c_int
+        lib.ddts_oracle_decode.argtypes = [ctypes.c_int] * 4 + [dp] * 8
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def fwd(q, k, v, g, tau, beta_hat, initial_state=None, return_final_state=True,
+        nthreads=0):
+    """Token-by-token fp64 forward over whole sequences.
+
+    q, k, g, tau: [B, T, H, dk]; v, beta_hat: [B, T, H, dv];
+    initial_state: [B, H, dk, dv] or None (zeros).
+    Returns (o [B, T, H, dv], S_T [B, H, dk, dv] or None), both float64.
+    The number of threads actually used is stored in ``fwd.last_threads``.
+    """
+    q, k, g, tau, v, beta_hat = map(_f64, (q, k, g, tau, v, beta_hat))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    for a in (k, g, tau):
+        assert a.shape == (B, T, H, dk)
+    for a in (beta_hat,):
+        assert a.shape == (B, T, H, dv)
+    s0 = None if initial_state is None else _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (B, H, dk, dv)
+    out = np.empty((B, T, H, dv), np.float64)
+    sf = np.empty((B, H, dk, dv), np.float64) if return_final_state else None
+    rc = _load().ddts_oracle_fwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(g), _ptr(tau),
+                                 _ptr(v), _ptr(beta_hat), _ptr(s0), _ptr(out), _ptr(sf),
+                                 int(nthreads))
+    if rc < 0:
+        raise RuntimeError("ddts_oracle_fwd failed")
+    fwd.last_threads = rc
+    return out, sf
+
+
+fwd.last_threads = 0
+
+
+def decode(q, k, v, g, tau, beta_hat, state):
+    """One fp64 recurrent step for N sequences.
+
+    q, k, g, tau: [N, H, dk]; v, beta_hat: [N, H, dv]; state: [N, H, dk, dv].
+    Returns (o [N, H, dv], new_state [N, H, dk, dv]); the input is not modified.
+    """
+    q, k, g, tau, v, beta_hat = map(_f64, (q, k, g, tau, v, beta_hat))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    assert st.shape == (N, H, dk, dv)
+    out = np.empty((N, H, dv), np.float64)
+    rc = _load().ddts_oracle_decode(N, H, dk, dv, _ptr(q), _ptr(k), _ptr(g), _ptr(tau),
+                                    _ptr(v), _ptr(beta_hat), _ptr(st), _ptr(out))
+    if rc < 0:
+        raise RuntimeError("ddts_oracle_decode failed")
+    return out, st
+
+
+def rel_to_rms_error(x_hat, x) -> float:
+    """max_i |x_hat_i - x_i| / sqrt(mean_i x_i^2): the parity metric."""
+    x = np.asarray(x, np.float64)
+    x_hat = np.asarray(x_hat, np.float64)
+    rms = float(np.sqrt(np.mean(x * x)))
+    if rms == 0.0:
+        return float(np.max(np.abs(x_hat - x))) if x.size else 0.0
+    return float(np.max(np.abs(x_hat - x))) / rms
