@@ -1,0 +1,183 @@
+"""MI355X (gfx950) DDTS gated linear-attention recurrence of Rodimus.
+
+Thin Python binding over the C ABI of ``librodimus_ddts.so`` (declared in
+``include/rodimus_ddts.h``).  This module only marshals arguments: it checks
+tensor shapes/dtypes/devices, allocates the outputs and the workspace with
+torch, and passes raw device pointers and the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+
+    o, S = chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None,
+                     output_final_state=False, chunk=0)
+    o = decode_step(q, k, v, g, tau, beta_hat, state)       # state updated in place
+
+Per head:  alpha = exp(-g*tau), alpha_hat = g**tau (over dk),
+S_t = diag(alpha_t) S_{t-1} + (alpha_hat_t*k_t)(beta_hat_t*v_t)^T, o_t = S_t^T q_t
+(gate formulas: Rodimus* digest page, "Method"; selection along n only:
+Rodimus* rebuttal page, "Efficient Parallelization").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "RodimusError",
+           "LIB_PATH", "abi_version"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librodimus_ddts.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+_lib = None
+
+
+class RodimusError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_linear_attention_rodimus_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.rodimus_abi_version.restype = i
+        L.rodimus_abi_version.argtypes = []
+        L.rodimus_status_string.restype = ctypes.c_char_p
+        L.rodimus_status_string.argtypes = [i]
+        L.rodimus_ddts_chunk_fwd_workspace_bytes.restype = sz
+        L.rodimus_ddts_chunk_fwd_workspace_bytes.argtypes = [i] * 6
+        L.rodimus_ddts_chunk_fwd_ex_workspace_bytes.restype = sz
+        L.rodimus_ddts_chunk_fwd_ex_workspace_bytes.argtypes = [i] * 7
+        L.rodimus_ddts_chunk_fwd.restype = i
+        L.rodimus_ddts_chunk_fwd.argtypes = [i] * 7 + [vp] * 9 + [vp, sz, vp]
+        L.rodimus_ddts_chunk_fwd_ex.restype = i
+        L.rodimus_ddts_chunk_fwd_ex.argtypes = [i] * 8 + [vp] * 9 + [vp, sz, vp]
+        L.rodimus_ddts_decode_step.restype = i
+        L.rodimus_ddts_decode_step.argtypes = [i] * 5 + [vp] * 8 + [vp]
+        _lib = L
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().rodimus_status_string(status).decode()
+    except Exception:
+        return "unknown"
+
+
+def abi_version() -> int:
+    return lib().rodimus_abi_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"per-token inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t.shape != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def workspace_bytes(B, T, H, dk, dv, chunk=0, segments=0) -> int:
+    return int(lib().rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, chunk, segments))
+
+
+def chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None, output_final_state=False,
+              chunk=0, segments=0, out=None, final_state=None, workspace=None):
+    """Chunkwise-parallel forward.  q, k, g, tau: [B, T, H, dk]; v, beta_hat:
+    [B, T, H, dv]; all six bf16 or all six fp32, contiguous, on one GPU.
+    initial_state: [B, H, dk, dv] fp32 or None.  Returns (o fp32 [B, T, H, dv],
+    final state fp32 [B, H, dk, dv] or None).  ``final_state`` may be passed
+    (also as the same tensor as ``initial_state``, for in-place carry-over)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd runs on the GPU only; inputs must be on a cuda device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("tau", tau, dk),
+                       ("v", v, dv), ("beta_hat", beta_hat, dv)):
+        _check_tensor(name, t, (B, T, H, d), dt, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, (B, T, H, dv), torch.float32, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_tensor("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    wsb = workspace_bytes(B, T, H, dk, dv, chunk, segments)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib().rodimus_ddts_chunk_fwd_ex(
+        B, T, H, dk, dv, int(chunk), int(segments), code,
+        _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat),
+        _ptr(initial_state), _ptr(out), _ptr(final_state),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_chunk_fwd")
+    return out, final_state
+
+
+def decode_step(q, k, v, g, tau, beta_hat, state, out=None):
+    """One recurrent step for N sequences.  q, k, g, tau: [N, H, dk]; v,
+    beta_hat: [N, H, dv]; state: [N, H, dk, dv] fp32, updated in place.
+    Returns o fp32 [N, H, dv]."""
+    torch = _torch()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_step runs on the GPU only; inputs must be on a cuda device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("tau", tau, dk),
+                       ("v", v, dv), ("beta_hat", beta_hat, dv)):
+        _check_tensor(name, t, (N, H, d), dt, dev)
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, (N, H, dv), torch.float32, dev)
+    st = lib().rodimus_ddts_decode_step(
+        N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat),
+        _ptr(state), _ptr(out), _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_decode_step")
+    return out

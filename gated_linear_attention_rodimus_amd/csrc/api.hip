@@ -1,0 +1,272 @@
+// api.hip -- the extern "C" boundary: argument validation, execution plan,
+// dispatch.  Every check runs on the host before any HIP call; nothing here
+// allocates device memory.
+#include "../../include/rodimus_ddts.h"
+#include "internal.h"
+
+#include <stdint.h>
+
+using namespace rodimus;
+
+namespace {
+
+constexpr size_t kLdsLimit = 160 * 1024;   // LDS per CU on gfx950
+constexpr int kTargetBlocks = 256;         // compute units on MI355X
+
+bool width_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Span span(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Pick chunk length, dv tile and segment count.  Returns false if no
+// instantiated tile shape fits the LDS for a user-fixed chunk.
+bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, bool f32,
+               ChunkPlan *P)
+{
+    const int chunks_try[3] = {64, 32, 16};
+    const int dvt_pref[3] = {64, 32, 16};
+    bool found = false;
+    for (int ci = 0; ci < 3 && !found; ++ci) {
+        const int C = chunks_try[ci];
+        if (chunk != 0 && C != chunk) continue;
+        for (int di = 0; di < 3 && !found; ++di) {
+            const int dvt = dvt_pref[di];
+            if (dvt > dv) continue;
+            const size_t lds = chunk_lds_bytes(dk, dvt, C, f32);
+            if (lds == 0 || lds > kLdsLimit) continue;
+            P->C = C;
+            P->DVT = dvt;
+            P->lds_bytes = lds;
+            found = true;
+        }
+    }
+    if (!found) return false;
+    P->n_chunks = T > 0 ? (T + P->C - 1) / P->C : 0;
+    const long long cols = (long long)B * H * (dv / P->DVT);
+    int seg = segments;
+    if (seg == 0) {
+        // one sweep per (b, h, dv tile) when that fills the GPU or the
+        // sequence is short; otherwise split the sequence into pieces of at
+        // least 8 chunks so that about kTargetBlocks workgroups run
+        seg = 1;
+        if (cols < kTargetBlocks / 2 && P->n_chunks >= 32) {
+            long long want = kTargetBlocks / cols;
+            long long cap = P->n_chunks / 8;
+            seg = (int)(want < cap ? want : cap);
+            if (seg < 1) seg = 1;
+        }
+    }
+    if (seg > P->n_chunks) seg = P->n_chunks > 0 ? P->n_chunks : 1;
+    if (seg < 1) seg = 1;
+    P->chunks_per_seg = P->n_chunks > 0 ? (P->n_chunks + seg - 1) / seg : 0;
+    // drop empty trailing segments
+    if (P->chunks_per_seg > 0) seg = (P->n_chunks + P->chunks_per_seg - 1) / P->chunks_per_seg;
+    P->segments = seg;
+    P->ws_bytes = seg > 1 ? (size_t)B * H * seg * ((size_t)dk * dv + dk) * sizeof(float) : 0;
+    return true;
+}
+
+rodimus_status check_chunk_args(int B, int T, int H, int dk, int dv, int chunk, int segments,
+                                rodimus_dtype dt)
+{
+    if (B <= 0 || H <= 0 || T < 0 || segments < 0) return RODIMUS_ERR_INVALID_ARG;
+    if (dt != RODIMUS_DTYPE_F32 && dt != RODIMUS_DTYPE_BF16) return RODIMUS_ERR_UNSUPPORTED;
+    if (!width_ok(dk) || !width_ok(dv)) return RODIMUS_ERR_UNSUPPORTED;
+    if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return RODIMUS_ERR_UNSUPPORTED;
+    // index arithmetic inside the kernels is 64-bit; keep the token count in int
+    if ((long long)B * T > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    return RODIMUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rodimus_abi_version(void) { return RODIMUS_ABI_VERSION; }
+
+const char *rodimus_status_string(rodimus_status s)
+{
+    switch (s) {
+    case RODIMUS_OK: return "ok";
+    case RODIMUS_ERR_INVALID_ARG: return "invalid argument";
+    case RODIMUS_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
+    case RODIMUS_ERR_WORKSPACE: return "workspace missing or too small";
+    case RODIMUS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                                 int segments)
+{
+    // dtype only changes the tile choice; report the larger of the two
+    size_t best = 0;
+    for (int f = 0; f < 2; ++f) {
+        if (check_chunk_args(B, T, H, dk, dv, chunk, segments,
+                             f ? RODIMUS_DTYPE_F32 : RODIMUS_DTYPE_BF16) != RODIMUS_OK)
+            return 0;
+        ChunkPlan P;
+        if (make_plan(B, T, H, dk, dv, chunk, segments, f != 0, &P) && P.ws_bytes > best)
+            best = P.ws_bytes;
+    }
+    return best;
+}
+
+size_t rodimus_ddts_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk)
+{
+    return rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, chunk, 0);
+}
+
+rodimus_status rodimus_ddts_chunk_fwd_ex(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    rodimus_status st = check_chunk_args(B, T, H, dk, dv, chunk, segments, in_dtype);
+    if (st != RODIMUS_OK) return st;
+    const bool f32 = in_dtype == RODIMUS_DTYPE_F32;
+    const size_t esz = f32 ? 4 : 2;
+    const size_t ntok = (size_t)B * T * H;
+    const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+
+    if (T > 0) {
+        const void *ins[6] = {q, k, g, tau, v, beta_hat};
+        for (const void *p : ins)
+            if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+        if (!out || !aligned16(out)) return RODIMUS_ERR_INVALID_ARG;
+    }
+    if (initial_state && !aligned16(initial_state)) return RODIMUS_ERR_INVALID_ARG;
+    if (final_state && !aligned16(final_state)) return RODIMUS_ERR_INVALID_ARG;
+
+    // aliasing: out may overlap nothing; final_state may equal initial_state
+    const Span s_in[6] = {span(q, ntok * dk * esz), span(k, ntok * dk * esz),
+                          span(g, ntok * dk * esz), span(tau, ntok * dk * esz),
+                          span(v, ntok * dv * esz), span(beta_hat, ntok * dv * esz)};
+    const Span s_out = span(out, ntok * dv * sizeof(float));
+    const Span s_s0 = span(initial_state, initial_state ? state_bytes : 0);
+    const Span s_sf = span(final_state, final_state ? state_bytes : 0);
+    if (T > 0) {
+        for (const Span &x : s_in)
+            if (overlap(s_out, x)) return RODIMUS_ERR_INVALID_ARG;
+        if (overlap(s_out, s_s0) || overlap(s_out, s_sf)) return RODIMUS_ERR_INVALID_ARG;
+    }
+    if (final_state) {
+        if (T > 0)
+            for (const Span &x : s_in)
+                if (overlap(s_sf, x)) return RODIMUS_ERR_INVALID_ARG;
+        if (initial_state && final_state != initial_state && overlap(s_sf, s_s0))
+            return RODIMUS_ERR_INVALID_ARG;
+    }
+
+    ChunkPlan P;
+    if (!make_plan(B, T, H, dk, dv, chunk, segments, f32, &P)) return RODIMUS_ERR_UNSUPPORTED;
+    if (P.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < P.ws_bytes) return RODIMUS_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RODIMUS_ERR_INVALID_ARG;
+        const Span s_ws = span(workspace, P.ws_bytes);
+        for (const Span &x : s_in)
+            if (overlap(s_ws, x)) return RODIMUS_ERR_INVALID_ARG;
+        if (overlap(s_ws, s_out) || overlap(s_ws, s_s0) || overlap(s_ws, s_sf))
+            return RODIMUS_ERR_INVALID_ARG;
+    }
+
+    // ---- launches (argument checks are complete)
+    hipError_t e = hipSuccess;
+    if (T == 0) {
+        if (final_state && final_state != initial_state)
+            e = launch_state_copy(initial_state, final_state, (size_t)B * H * dk * dv, stream);
+        return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+    }
+    ChunkLaunch Lc;
+    Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv;
+    Lc.C = P.C; Lc.DVT = P.DVT; Lc.chunks_per_seg = P.chunks_per_seg;
+    Lc.f32_inputs = f32;
+    Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
+    Lc.gam_out = nullptr;
+    const long long sz = (long long)dk * dv;
+    if (P.segments == 1) {
+        Lc.n_seg = 1; Lc.mode = 0;
+        Lc.s_in = initial_state; Lc.s_in_bh_stride = sz; Lc.s_in_seg_stride = 0;
+        Lc.out = out;
+        Lc.s_out = final_state; Lc.s_out_bh_stride = sz; Lc.s_out_seg_stride = 0;
+        Lc.s_out_last_only = 0;
+        e = launch_chunk(Lc, stream);
+        return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+    }
+    // segmented: (1) per-segment transfers from a zero state, (2) ordered
+    // combination into each segment's incoming state, (3) outputs.
+    const int n_seg = P.segments;
+    float *ws_ds = (float *)workspace;                                // [BH][P][dk][dv]
+    float *ws_gam = ws_ds + (size_t)B * H * n_seg * dk * dv;          // [BH][P][dk]
+    Lc.n_seg = n_seg; Lc.mode = 1;
+    Lc.s_in = nullptr; Lc.s_in_bh_stride = 0; Lc.s_in_seg_stride = 0;
+    Lc.out = nullptr;
+    Lc.s_out = ws_ds; Lc.s_out_bh_stride = (long long)n_seg * sz; Lc.s_out_seg_stride = sz;
+    Lc.s_out_last_only = 0;
+    Lc.gam_out = ws_gam;
+    e = launch_chunk(Lc, stream);
+    if (e != hipSuccess) return RODIMUS_ERR_HIP;
+    // final state: the output pass's last segment writes it (from its true S_in)
+    e = launch_segment_combine(B * H, n_seg, dk, dv, initial_state, ws_ds, ws_gam, nullptr, stream);
+    if (e != hipSuccess) return RODIMUS_ERR_HIP;
+    Lc.mode = 0;
+    Lc.s_in = ws_ds; Lc.s_in_bh_stride = (long long)n_seg * sz; Lc.s_in_seg_stride = sz;
+    Lc.out = out;
+    Lc.s_out = final_state; Lc.s_out_bh_stride = sz; Lc.s_out_seg_stride = 0;
+    Lc.s_out_last_only = 1;
+    Lc.gam_out = nullptr;
+    e = launch_chunk(Lc, stream);
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+rodimus_status rodimus_ddts_chunk_fwd(
+    int B, int T, int H, int dk, int dv, int chunk, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return rodimus_ddts_chunk_fwd_ex(B, T, H, dk, dv, chunk, 0, in_dtype, q, k, g, tau, v, beta_hat,
+                                     initial_state, out, final_state, workspace, workspace_bytes,
+                                     stream);
+}
+
+rodimus_status rodimus_ddts_decode_step(
+    int N, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    float *state, float *out, hipStream_t stream)
+{
+    if (N <= 0 || H <= 0) return RODIMUS_ERR_INVALID_ARG;
+    if (in_dtype != RODIMUS_DTYPE_F32 && in_dtype != RODIMUS_DTYPE_BF16) return RODIMUS_ERR_UNSUPPORTED;
+    if (!width_ok(dk) || !width_ok(dv)) return RODIMUS_ERR_UNSUPPORTED;
+    if ((long long)N * H > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    const void *ins[6] = {q, k, g, tau, v, beta_hat};
+    for (const void *p : ins)
+        if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+    if (!state || !out || !aligned16(state) || !aligned16(out)) return RODIMUS_ERR_INVALID_ARG;
+    const size_t esz = in_dtype == RODIMUS_DTYPE_F32 ? 4 : 2;
+    const size_t pairs = (size_t)N * H;
+    const Span s_st = span(state, pairs * dk * dv * sizeof(float));
+    const Span s_o = span(out, pairs * dv * sizeof(float));
+    const Span s_in[6] = {span(q, pairs * dk * esz), span(k, pairs * dk * esz),
+                          span(g, pairs * dk * esz), span(tau, pairs * dk * esz),
+                          span(v, pairs * dv * esz), span(beta_hat, pairs * dv * esz)};
+    if (overlap(s_st, s_o)) return RODIMUS_ERR_INVALID_ARG;
+    for (const Span &x : s_in)
+        if (overlap(s_st, x) || overlap(s_o, x)) return RODIMUS_ERR_INVALID_ARG;
+    hipError_t e = launch_decode(N, H, dk, dv, in_dtype == RODIMUS_DTYPE_F32,
+                                 TokenInputs{q, k, g, tau, v, beta_hat}, state, out, stream);
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+}  // extern "C"

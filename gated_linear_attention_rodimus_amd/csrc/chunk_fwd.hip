@@ -1,0 +1,103 @@
+// chunk_fwd.hip -- dispatch of the chunk-forward kernels by dk, and the two
+// small kernels of the segmented path: the ordered combination of segment
+// state transfers and the state copy used when T == 0.
+//
+// Segmented path (long sequences with few heads): the sequence of one (b, h)
+// is cut into P pieces.  Chaining the recurrence over a piece from state X
+// gives diag(G_p) X + dS_p, where G_p is the product of the piece's forget
+// gates and dS_p the piece's result from a zero state.  These affine maps
+// compose in order, so S_in[p] = diag(G_{p-1}) S_in[p-1] + dS_{p-1}; the
+// pieces then run in parallel from their true incoming states.  This only
+// reorders the recurrence's own products and sums (the chunkwise-parallel
+// training form of the rebuttal page, paperhub.cn, answer on sequential
+// processing bottlenecks).
+#include "internal.h"
+
+namespace rodimus {
+
+size_t chunk_lds_bytes_dk16(int, int, bool);
+size_t chunk_lds_bytes_dk32(int, int, bool);
+size_t chunk_lds_bytes_dk64(int, int, bool);
+size_t chunk_lds_bytes_dk128(int, int, bool);
+hipError_t launch_chunk_dk16(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk32(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk64(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk128(const ChunkLaunch &, hipStream_t);
+
+namespace {
+
+// ---------------------------------------------------------------- segment combine
+// S_in[0] = S0 (or 0); S_in[p] = diag(gam[p-1]) S_in[p-1] + dS[p-1]; written in
+// place over dS.  One thread per state element, sequential over segments.
+__global__ __launch_bounds__(256) void segment_combine_kernel(
+    int n_seg, int dk, int dv, const float *__restrict__ s0, float *__restrict__ ds,
+    const float *__restrict__ gam, float *__restrict__ final_state)
+{
+    const int bh = blockIdx.y;
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= dk * dv) return;
+    const int i = e / dv;
+    const size_t st = (size_t)dk * dv;
+    float run = s0 ? s0[(size_t)bh * st + e] : 0.f;
+    float *d = ds + (size_t)bh * n_seg * st + e;
+    const float *gm = gam + (size_t)bh * n_seg * dk + i;
+    for (int p = 0; p < n_seg; ++p) {
+        const float dsp = d[(size_t)p * st];
+        d[(size_t)p * st] = run;
+        run = gm[(size_t)p * dk] * run + dsp;
+    }
+    if (final_state) final_state[(size_t)bh * st + e] = run;
+}
+
+__global__ __launch_bounds__(256) void state_copy_kernel(const float *__restrict__ src,
+                                                         float *__restrict__ dst, size_t n)
+{
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n) dst[e] = src ? src[e] : 0.f;
+}
+
+}  // namespace
+
+size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs)
+{
+    switch (dk) {
+    case 16: return chunk_lds_bytes_dk16(dvt, C, f32_inputs);
+    case 32: return chunk_lds_bytes_dk32(dvt, C, f32_inputs);
+    case 64: return chunk_lds_bytes_dk64(dvt, C, f32_inputs);
+    case 128: return chunk_lds_bytes_dk128(dvt, C, f32_inputs);
+    }
+    return 0;
+}
+
+hipError_t launch_chunk(const ChunkLaunch &Lc, hipStream_t stream)
+{
+    switch (Lc.dk) {
+    case 16: return launch_chunk_dk16(Lc, stream);
+    case 32: return launch_chunk_dk32(Lc, stream);
+    case 64: return launch_chunk_dk64(Lc, stream);
+    case 128: return launch_chunk_dk128(Lc, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_segment_combine(int BH, int n_seg, int dk, int dv, const float *s0,
+                                  float *ds_inout, const float *gam, float *final_state,
+                                  hipStream_t stream)
+{
+    const int elems = dk * dv;
+    dim3 grid((elems + 255) / 256, BH);
+    hipLaunchKernelGGL(segment_combine_kernel, grid, dim3(256), 0, stream, n_seg, dk, dv, s0,
+                       ds_inout, gam, final_state);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStream_t stream)
+{
+    if (count == 0) return hipSuccess;
+    const size_t blocks = (count + 255) / 256;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst,
+                       count);
+    return hipGetLastError();
+}
+
+}  // namespace rodimus

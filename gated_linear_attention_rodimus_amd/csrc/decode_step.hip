@@ -1,0 +1,154 @@
+// decode_step.hip -- one recurrent DDTS step over a batch of resident states.
+//
+// Sequential inference over a cached fixed-size state (Rodimus* rebuttal page,
+// paperhub.cn, answer on sequential processing bottlenecks): per (n, h)
+//   S <- diag(exp(-g*tau)) S + (g^tau * k)(beta_hat * v)^T,   o = S^T q
+// with the gates of the Rodimus* digest page (digest.lyk-ai.com), "Method".
+//
+// The step is bound by HBM: the fp32 state (dk*dv*4 bytes per head) is read
+// and written once, the inputs are ~3% of the traffic.  One workgroup of 256
+// threads owns one (or, for small heads, several) state slices:
+//  - each thread owns one float4 column group c (dv/4 of them per row) and a
+//    fixed set of rows, so every wave-wide load or store touches whole 128-byte
+//    lines (coalesced 128-bit accesses), all loads issued before any math;
+//  - per-row gates (alpha_i, alpha_hat_i*k_i) and per-column v'_j are computed
+//    once per slice into LDS while the state loads are in flight;
+//  - o_j = sum_i q_i S_ij is reduced over the row groups through LDS.
+#include "internal.h"
+
+namespace rodimus {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float ld_in(const __bf16 *p, size_t i) { return (float)p[i]; }
+__device__ __forceinline__ float ld_in(const float *p, size_t i) { return p[i]; }
+
+// alpha_hat = g^tau with pow semantics at g = 0 (0^0 = 1, 0^tau = 0).
+__device__ __forceinline__ float gate_pow(float g, float tau) {
+    if (g > 0.f) return __builtin_amdgcn_exp2f(tau * __builtin_amdgcn_logf(g));
+    return tau == 0.f ? 1.f : 0.f;
+}
+
+template <int DK, int DV, typename TIn>
+__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+    int pairs, const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ g,
+    const TIn *__restrict__ tau, const TIn *__restrict__ v, const TIn *__restrict__ beta,
+    float *__restrict__ state, float *__restrict__ out)
+{
+    constexpr int CG = DV / 4;                       // float4 column groups per row
+    constexpr int F4 = DK * DV / 4;                  // float4s per slice
+    constexpr int PPB = F4 >= kThreads ? 1 : kThreads / F4;   // slices per block
+    constexpr int TPP = kThreads / PPB;              // threads per slice
+    constexpr int PER = F4 / TPP;                    // float4s per thread
+    constexpr int RG = TPP / CG;                     // row groups per slice
+    static_assert(PER >= 1 && F4 % TPP == 0 && TPP % CG == 0, "tile shape");
+
+    __shared__ float s_a[PPB][DK], s_kk[PPB][DK], s_q[PPB][DK], s_vv[PPB][DV];
+    __shared__ float s_red[PPB][RG][DV];
+
+    const int t = threadIdx.x;
+    const int slot = t / TPP, lt = t % TPP;
+    const int pair = blockIdx.x * PPB + slot;
+    const bool active = pair < pairs;
+    const int c = lt % CG, rg = lt / CG;
+
+    float4 *S = reinterpret_cast<float4 *>(state) + (size_t)(active ? pair : 0) * F4;
+    float4 s[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+        s[m] = active ? S[lt + m * TPP] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // gates for this slice (rows over dk, columns over dv)
+    if (active) {
+        const size_t rk = (size_t)pair * DK, rv = (size_t)pair * DV;
+        for (int i = lt; i < DK; i += TPP) {
+            const float gi = ld_in(g, rk + i), ti = ld_in(tau, rk + i);
+            s_a[slot][i] = __builtin_amdgcn_exp2f(-gi * ti * kLog2e);
+            s_kk[slot][i] = gate_pow(gi, ti) * ld_in(k, rk + i);
+            s_q[slot][i] = ld_in(q, rk + i);
+        }
+        for (int j = lt; j < DV; j += TPP)
+            s_vv[slot][j] = ld_in(beta, rv + j) * ld_in(v, rv + j);
+    }
+    __syncthreads();
+
+    if (active) {
+        const float v0 = s_vv[slot][4 * c], v1 = s_vv[slot][4 * c + 1];
+        const float v2 = s_vv[slot][4 * c + 2], v3 = s_vv[slot][4 * c + 3];
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int i = rg + m * RG;               // row of this float4
+            const float a = s_a[slot][i], kk = s_kk[slot][i], qi = s_q[slot][i];
+            float4 x = s[m];
+            x.x = a * x.x + kk * v0;
+            x.y = a * x.y + kk * v1;
+            x.z = a * x.z + kk * v2;
+            x.w = a * x.w + kk * v3;
+            S[lt + m * TPP] = x;
+            o0 += qi * x.x; o1 += qi * x.y; o2 += qi * x.z; o3 += qi * x.w;
+        }
+        s_red[slot][rg][4 * c] = o0;
+        s_red[slot][rg][4 * c + 1] = o1;
+        s_red[slot][rg][4 * c + 2] = o2;
+        s_red[slot][rg][4 * c + 3] = o3;
+    }
+    __syncthreads();
+    if (active) {
+        for (int j = lt; j < DV; j += TPP) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) acc += s_red[slot][r][j];
+            out[(size_t)pair * DV + j] = acc;
+        }
+    }
+}
+
+template <int DK, int DV, typename TIn>
+hipError_t launch_typed(int pairs, const TokenInputs &in, float *state, float *out,
+                        hipStream_t stream)
+{
+    constexpr int F4 = DK * DV / 4;
+    constexpr int PPB = F4 >= kThreads ? 1 : kThreads / F4;
+    const int blocks = (pairs + PPB - 1) / PPB;
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn>), dim3(blocks), dim3(kThreads), 0, stream,
+                       pairs, (const TIn *)in.q, (const TIn *)in.k, (const TIn *)in.g,
+                       (const TIn *)in.tau, (const TIn *)in.v, (const TIn *)in.beta, state, out);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_dtype(int pairs, int dk, int dv, const TokenInputs &in, float *state,
+                        float *out, hipStream_t stream)
+{
+#define RODIMUS_DEC_DV(DK)                                                              \
+    switch (dv) {                                                                       \
+    case 16: return launch_typed<DK, 16, TIn>(pairs, in, state, out, stream);           \
+    case 32: return launch_typed<DK, 32, TIn>(pairs, in, state, out, stream);           \
+    case 64: return launch_typed<DK, 64, TIn>(pairs, in, state, out, stream);           \
+    case 128: return launch_typed<DK, 128, TIn>(pairs, in, state, out, stream);         \
+    }                                                                                   \
+    break;
+    switch (dk) {
+    case 16: RODIMUS_DEC_DV(16)
+    case 32: RODIMUS_DEC_DV(32)
+    case 64: RODIMUS_DEC_DV(64)
+    case 128: RODIMUS_DEC_DV(128)
+    }
+#undef RODIMUS_DEC_DV
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
+                         float *state, float *out, hipStream_t stream)
+{
+    const int pairs = N * H;
+    return f32_inputs ? launch_dtype<float>(pairs, dk, dv, in, state, out, stream)
+                      : launch_dtype<__bf16>(pairs, dk, dv, in, state, out, stream);
+}
+
+}  // namespace rodimus

@@ -1,0 +1,57 @@
+// internal.h -- declarations shared by the library's translation units
+// (host-side launchers; kernels stay private to their .hip file).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace rodimus {
+
+// Per-token input pointers (device), typed as the storage dtype by the kernels.
+struct TokenInputs {
+    const void *q, *k, *g, *tau, *v, *beta;
+};
+
+// How one chunk-forward call is executed.
+struct ChunkPlan {
+    int C;          // tokens per chunk
+    int DVT;        // dv columns per workgroup
+    int segments;   // pieces per (b, h) sequence run in parallel (1 = one sweep)
+    int n_chunks;   // ceil(T / C)
+    int chunks_per_seg;
+    size_t lds_bytes;
+    size_t ws_bytes;
+};
+
+// Bytes of LDS the chunk kernel needs for a tile shape (0 if not instantiated).
+size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs);
+
+// Chunk sweep / segment pass.  mode 0: outputs from S_in; mode 1: segment
+// state transfer (dS from a zero state, and the product of decays).
+struct ChunkLaunch {
+    int B, T, H, dk, dv;
+    int C, DVT, n_seg, chunks_per_seg;
+    int mode;
+    bool f32_inputs;
+    TokenInputs in;
+    const float *s_in; long long s_in_bh_stride, s_in_seg_stride;
+    float *out;
+    float *s_out; long long s_out_bh_stride, s_out_seg_stride; int s_out_last_only;
+    float *gam_out;         // [B*H][n_seg][dk] (mode 1)
+};
+hipError_t launch_chunk(const ChunkLaunch &L, hipStream_t stream);
+
+// Ordered combination of segment transfers: S_in[p] for every segment, in
+// place over dS, plus optionally the final state.
+hipError_t launch_segment_combine(int BH, int n_seg, int dk, int dv, const float *s0,
+                                  float *ds_inout, const float *gam, float *final_state,
+                                  hipStream_t stream);
+
+// Copy or zero a [count] fp32 array (T == 0 forwards).
+hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStream_t stream);
+
+hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
+                         float *state, float *out, hipStream_t stream);
+
+}  // namespace rodimus

@@ -1,0 +1,155 @@
+/*
+ * rodimus_ddts.h -- C ABI of the MI355X (gfx950) DDTS recurrence library.
+ *
+ * The operation (per batch element b and head h; dk = expansion factor n,
+ * dv = value width m):
+ *
+ *   alpha_t     = exp(-g_t * tau_t)            forget gate, over dk
+ *   alpha_hat_t = g_t ^ tau_t                   input gate, over dk
+ *   S_t = diag(alpha_t) S_{t-1} + (alpha_hat_t * k_t) (beta_hat_t * v_t)^T
+ *   o_t = S_t^T q_t                             readout after the update
+ *
+ * Cited from the pages on Rodimus* (arXiv 2410.06577):
+ *  - gate formulas alpha = exp(-g*tau), alpha_hat = g^tau: the digest page
+ *    (digest.lyk-ai.com), section "Method";
+ *  - beta_hat is the low-rank gate on the value side: same section;
+ *  - selection acts only along n (the dk rows of S), which is what allows the
+ *    chunkwise-parallel form: the authors' rebuttal (paperhub.cn), bullet
+ *    "Efficient Parallelization";
+ *  - training runs chunkwise in parallel and inference sequentially over a
+ *    cached fixed-size state: the same rebuttal, answer on sequential
+ *    processing bottlenecks (Q2 of the first review);
+ *  - the state is n x m per head: the same rebuttal, answer on the
+ *    "State size n x m" column of Table 4.
+ * The recurrence's own equation (the paper's Eq. 11) is not on the pages; the
+ * readout-after-update order and the absence of any scaling of q inside the
+ * operation are the readings taken.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no memory and keeps no state; calls are reentrant.  Work is
+ *    enqueued on `stream` and the call returns before it completes.
+ *  - Every argument check happens on the host, synchronously, BEFORE any HIP
+ *    call; a failed check returns a status and enqueues nothing.
+ *  - Layouts are dense row-major: per-token tensors [B, T, H, D] with the
+ *    feature dimension contiguous; states [B, H, dk, dv] fp32 with dv
+ *    contiguous (the same layout for prefill and decode, so a prefill's final
+ *    state is a decode state).
+ *  - Supported widths: dk, dv in {16, 32, 64, 128}.  Pointers must be 16-byte
+ *    aligned.
+ *  - Domain (documented, not checked on the device): g >= 0 and tau >= 0.
+ *    NaN and Inf propagate.  The chunked form multiplies by exp(+-partial
+ *    sums of g*tau) inside a chunk; results are exact up to rounding while the
+ *    sum of g*tau over any half chunk stays below about 80 (true for gates in
+ *    [0, 1] at any supported chunk size).
+ */
+#ifndef RODIMUS_DDTS_H
+#define RODIMUS_DDTS_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RODIMUS_ABI_VERSION 1
+
+typedef enum {
+    RODIMUS_OK = 0,
+    RODIMUS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, overlap */
+    RODIMUS_ERR_UNSUPPORTED = 2,   /* width, chunk or dtype outside the supported set */
+    RODIMUS_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    RODIMUS_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} rodimus_status;
+
+typedef enum {
+    RODIMUS_DTYPE_F32 = 0,
+    RODIMUS_DTYPE_BF16 = 1
+} rodimus_dtype;
+
+/* ABI version of the loaded library (RODIMUS_ABI_VERSION). */
+int rodimus_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char *rodimus_status_string(rodimus_status status);
+
+/*
+ * Bytes of device workspace rodimus_ddts_chunk_fwd needs for these sizes
+ * (0 when the single-sweep path is used).  Returns 0 as well for arguments
+ * the forward would reject.  Deterministic: depends only on the arguments.
+ */
+size_t rodimus_ddts_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk);
+
+/*
+ * Chunkwise-parallel forward (prefill / training pass) over whole sequences.
+ *
+ *   B, T, H, dk, dv  sizes; B, H >= 1, T >= 0 (T == 0 only copies the state).
+ *   chunk            tokens per chunk: 0 = library's choice, else 16, 32 or 64.
+ *                    Results do not depend on it beyond rounding.
+ *   in_dtype         dtype of all six per-token inputs (bf16 or fp32); the
+ *                    state and the output are always fp32.
+ *   q, k, g, tau     [B, T, H, dk]
+ *   v, beta_hat      [B, T, H, dv]
+ *   initial_state    [B, H, dk, dv] fp32, or NULL for a zero state.
+ *   out              [B, T, H, dv] fp32; must not overlap any input or state.
+ *   final_state      [B, H, dk, dv] fp32, or NULL.  May be the same pointer as
+ *                    initial_state (carry-over in place), may not overlap it
+ *                    partially, and may not overlap any other tensor.
+ *   workspace        device scratch of at least
+ *                    rodimus_ddts_chunk_fwd_workspace_bytes(...) bytes (NULL
+ *                    allowed when that is 0); its contents on entry are ignored.
+ *   stream           HIP stream the kernels are launched on.
+ *
+ * Returns RODIMUS_OK, or an error status with nothing enqueued (argument
+ * errors) or with a HIP launch error (RODIMUS_ERR_HIP).
+ */
+rodimus_status rodimus_ddts_chunk_fwd(
+    int B, int T, int H, int dk, int dv, int chunk, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * As rodimus_ddts_chunk_fwd, with the sequence split into `segments` pieces
+ * per (b, h) that run in parallel: each piece's state transfer is computed
+ * from a zero state, the transfers are combined in order, and each piece then
+ * produces its outputs from its true incoming state.  segments = 0 lets the
+ * library choose (what rodimus_ddts_chunk_fwd does); 1 forces one sequential
+ * sweep per (b, h); values above the number of chunks are clamped.
+ * Workspace: rodimus_ddts_chunk_fwd_ex_workspace_bytes with the same arguments.
+ */
+rodimus_status rodimus_ddts_chunk_fwd_ex(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                                 int chunk, int segments);
+
+/*
+ * One recurrent step (sequential inference) for N independent sequences over
+ * their resident states, updated in place.
+ *
+ *   N, H, dk, dv     sizes; N, H >= 1.
+ *   in_dtype         dtype of the six per-token inputs.
+ *   q, k, g, tau     [N, H, dk]
+ *   v, beta_hat      [N, H, dv]
+ *   state            [N, H, dk, dv] fp32, read and overwritten with S_t.
+ *   out              [N, H, dv] fp32 (o_t); must not overlap the state or inputs.
+ *   stream           HIP stream.
+ */
+rodimus_status rodimus_ddts_decode_step(
+    int N, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    float *state, float *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RODIMUS_DDTS_H */
