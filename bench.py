@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the DDTS hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one chunkwise-parallel forward (rodimus_ddts_chunk_fwd) over one
+batch of the 130M-scale layer workload: B=8 sequences x T=2048 tokens x H=12
+heads, dk=64, dv=128, bf16 inputs, fp32 outputs.  Inputs are seeded synthetic
+tensors, resident in HBM before the timed region; the step cycles through
+``--rotate`` copies of them so that the 256 MB last-level cache cannot serve a
+batch from the previous step.  After the chunk steps the same run times
+``--decode-steps`` back-to-back decode steps over 256 x 16 resident fp32
+states (the batched decode workload) and reports the state bandwidth.
+
+One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
+per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
+launch / its HIP-event-timed duration), the decode-step bandwidth, and the
+fp64 CPU oracle timed on this host on the same workload (a reported baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "DDTS chunk-fwd tokens/s + % MFMA/HBM roofline; decode-step state GB/s"
+NAMES = ("q", "k", "v", "g", "tau", "beta_hat")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer130m_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_linear_attention_rodimus_amd", "csrc", "chunk_kernel.h")
+
+
+def chunk_algorithmic(B, T, H, dk, dv, C, in_bytes=2, state_in=False, state_out=False):
+    """Bytes the method must move and flops it must do (causal triangle once)."""
+    ntok = B * T * H
+    by = ntok * ((4 * dk + 2 * dv) * in_bytes + 4 * dv)
+    by += (int(state_in) + int(state_out)) * B * H * dk * dv * 4
+    fl = ntok * ((C + 1) * (dk + dv) + 4 * dk * dv)
+    return by, fl
+
+
+def decode_algorithmic(N, H, dk, dv, in_bytes=2):
+    by = 2 * N * H * dk * dv * 4 + N * H * (4 * dk + 2 * dv) * in_bytes + N * H * dv * 4
+    return by, 5 * N * H * dk * dv
+
+
+def kernel_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=3, help="input copies cycled over steps")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="layer130m")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ddts_inputs as D
+    import gated_linear_attention_rodimus_amd as R
+
+    dev = torch.device("cuda:0")
+    wl = D.WORKLOADS[args.workload]
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    x = D.make(args.workload)
+    sets = []
+    for r in range(max(1, args.rotate)):
+        t = [x.torch(n, dev) for n in NAMES]
+        if r:
+            t = [a.clone() for a in t]
+        out = torch.empty(B, T, H, dv, device=dev)
+        fs = torch.empty(B, H, dk, dv, device=dev) if wl.final_state else None
+        s0 = torch.from_numpy(x.initial_state).to(dev) if x.initial_state is not None else None
+        sets.append((t, s0, out, fs))
+    wsb = R.workspace_bytes(B, T, H, dk, dv)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    torch.cuda.synchronize()
+
+    def step(i):
+        t, s0, out, fs = sets[i % len(sets)]
+        R.chunk_fwd(*t, initial_state=s0, out=out, final_state=fs, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = 1e3 * wall / args.steps
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    tokens = B * T
+    value = tokens * args.steps / wall
+
+    C = 64
+    abytes, aflops = chunk_algorithmic(B, T, H, dk, dv, C, state_in=x.initial_state is not None,
+                                       state_out=wl.final_state)
+    achieved = abytes / avg_launch_s / 1e9
+    traffic = kernel_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic,
+                "kernel": "chunk_fwd_kernel<64,64,64,bf16>" if wsb == 0 else "chunk_fwd (segmented)",
+                "algorithmic_bytes_per_launch": abytes,
+                "launch_us": round(avg_launch_s * 1e6, 2),
+                "mfma": {"achieved_tflops": round(aflops / avg_launch_s / 1e12, 2),
+                         "peak_tflops": BF16_PEAK_TFLOPS,
+                         "frac": round(aflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops_per_launch": aflops}}
+
+    # ---------------- decode: back-to-back steps over resident states
+    decode = None
+    if args.decode_steps > 0:
+        dsets, st = D.make_decode_pool("decode_batch")
+        N, Hd, dkd, dvd = st.shape
+        dins = [[s.torch(n, dev)[:, 0] for n in NAMES] for s in dsets]
+        S = torch.from_numpy(st).to(dev)
+        o = torch.empty(N, Hd, dvd, device=dev)
+        for i in range(10):
+            R.decode_step(*dins[i % len(dins)], S, out=o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            R.decode_step(*dins[i % len(dins)], S, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        dbytes, dflops = decode_algorithmic(N, Hd, dkd, dvd)
+        # cold variant: three state batches in rotation (384 MiB > last-level cache)
+        Ss = [S] + [S.clone() for _ in range(2)]
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            R.decode_step(*dins[i % len(dins)], Ss[i % 3], out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_cold = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        decode = {"workload": f"decode_batch N{N} H{Hd} dk{dkd} dv{dvd} bf16 inputs, fp32 state",
+                  "steps": args.decode_steps, "us_per_step": round(us, 2),
+                  "algorithmic_bytes_per_step": dbytes,
+                  "state_GBps": round(2 * N * Hd * dkd * dvd * 4 / us / 1e3, 1),
+                  "algorithmic_GBps": round(dbytes / us / 1e3, 1),
+                  "frac_hbm": round(dbytes / us / 1e3 / HBM_PEAK_GBPS, 4),
+                  "cold_us_per_step": round(us_cold, 2),
+                  "cold_algorithmic_GBps": round(dbytes / us_cold / 1e3, 1),
+                  "tokens_per_s": round(N / (us * 1e-6), 1)}
+
+    # ---------------- CPU baseline: the fp64 oracle on this host, same workload
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        # bounded sample: all heads of the first sequences, whole length
+        Bs = B
+        ins = [np.ascontiguousarray(x.f32(n)[:Bs]) for n in NAMES]
+        s0 = None if x.initial_state is None else x.initial_state[:Bs]
+        c0 = time.perf_counter()
+        ro, _ = oracle.fwd(*ins, s0, nthreads=nthreads)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(Bs * T / cs, 1), "unit": "tokens/s", "cores": oracle.fwd.last_threads,
+               "kind": "oracle",
+               "sample": f"{Bs} of {B} sequences x {T} tokens x {H} heads of the same workload, "
+                         f"fp64 C oracle, {cs:.2f} s"}
+        gpu_o = sets[0][2][:Bs].cpu().numpy()
+        parity = {"max_abs_over_rms": oracle.rel_to_rms_error(gpu_o, ro), "bar": 1e-2,
+                  "sample": "the CPU-baseline sample"}
+
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{args.workload}: B={B} T={T} H={H} dk={dk} dv={dv} "
+                                   f"bf16 inputs, fp32 out/state, chunk {C}",
+                       "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
+                       "rotating_input_sets": len(sets), "parallelism": "single GPU"},
+            "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "parity": parity}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,9 +67,13 @@ DECODE_POOL = 16   # distinct input sets cycled over decode steps
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    t += u                       # no overflow for finite inputs (|x| <= FLT_MAX)
+    t >>= 16
+    r = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
@@ -82,7 +86,13 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _sigmoid32(x):
-    return (1.0 / (1.0 + np.exp(-x, dtype=np.float32))).astype(np.float32)
+    """1 / (1 + exp(-x)) in float32, computed in place (x is consumed)."""
+    x = np.asarray(x, dtype=np.float32)
+    np.negative(x, out=x)
+    np.exp(x, out=x)
+    x += np.float32(1.0)
+    np.reciprocal(x, out=x)
+    return x
 
 
 @dataclasses.dataclass
@@ -151,9 +161,14 @@ def make(name: str, sub: int = 0, **overrides) -> Inputs:
             x += np.float32(mean)
         return x
 
-    q = _encode(normal(_Q, sk) * inv, wl.dtype)
-    k = _encode(normal(_K, sk) * inv, wl.dtype)
-    v = _encode(normal(_V, sv) * inv, wl.dtype)
+    def scaled(tid, shape):
+        x = normal(tid, shape)
+        x *= inv
+        return x
+
+    q = _encode(scaled(_Q, sk), wl.dtype)
+    k = _encode(scaled(_K, sk), wl.dtype)
+    v = _encode(scaled(_V, sv), wl.dtype)
     g = _encode(_sigmoid32(normal(_G, sk, mean=wl.g_mean)), wl.dtype)
     tau = _encode(_sigmoid32(normal(_TAU, sk)), wl.dtype)
     if wl.beta == "rank16":

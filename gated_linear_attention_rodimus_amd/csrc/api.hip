@@ -33,9 +33,11 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     const int chunks_try[3] = {64, 32, 16};
     const int dvt_pref[3] = {64, 32, 16};
     bool found = false;
+    // a requested chunk length is an upper bound: a shorter chunk is used only
+    // where that tile shape does not fit in LDS (fp32 inputs at dk = 128)
     for (int ci = 0; ci < 3 && !found; ++ci) {
         const int C = chunks_try[ci];
-        if (chunk != 0 && C != chunk) continue;
+        if (chunk != 0 && C > chunk) continue;
         for (int di = 0; di < 3 && !found; ++di) {
             const int dvt = dvt_pref[di];
             if (dvt > dv) continue;

@@ -1,0 +1,159 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call (no GPU needed: every
+call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_attention_rodimus_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rodimus_ddts.h")
+
+# fake, 16-byte aligned, never dereferenced device addresses
+BASE = 0x7F0000000000
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rodimus_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert "rodimus_ddts_chunk_fwd" in names and "rodimus_ddts_decode_step" in names
+    L = ctypes.CDLL(R.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in rodimus_ddts.h but not exported"
+
+
+def test_version_and_status_strings():
+    assert R.abi_version() == 1
+    L = R.lib()
+    for s in range(5):
+        assert L.rodimus_status_string(s)
+    assert L.rodimus_status_string(0) == b"ok"
+
+
+def _chunk(B=1, T=128, H=2, dk=64, dv=128, chunk=0, segments=0, dtype=R.DTYPE_BF16,
+           ptrs=None, s0=None, out=None, sf=None, ws=None, wsb=0):
+    esz = 4 if dtype == R.DTYPE_F32 else 2
+    ntok = B * T * H
+    if ptrs is None:
+        ptrs = []
+        a = BASE
+        for d in (dk, dk, dk, dk, dv, dv):
+            ptrs.append(a)
+            a += ((ntok * d * esz + MB) // 16) * 16
+        if out is None:
+            out = a
+    vp = ctypes.c_void_p
+    return R.lib().rodimus_ddts_chunk_fwd_ex(
+        B, T, H, dk, dv, chunk, segments, dtype, *(vp(p) if p else None for p in ptrs),
+        vp(s0) if s0 else None, vp(out) if out else None, vp(sf) if sf else None,
+        vp(ws) if ws else None, wsb, None)
+
+
+def test_chunk_rejects_bad_sizes():
+    assert _chunk(B=0) == R.ERR_INVALID_ARG
+    assert _chunk(H=0) == R.ERR_INVALID_ARG
+    assert _chunk(T=-1) == R.ERR_INVALID_ARG
+    assert _chunk(segments=-1) == R.ERR_INVALID_ARG
+    assert _chunk(dk=48) == R.ERR_UNSUPPORTED
+    assert _chunk(dv=256) == R.ERR_UNSUPPORTED
+    assert _chunk(chunk=8) == R.ERR_UNSUPPORTED
+    assert _chunk(chunk=128) == R.ERR_UNSUPPORTED
+    assert _chunk(dtype=7) == R.ERR_UNSUPPORTED
+
+
+def test_chunk_rejects_bad_pointers():
+    good = [BASE + i * 64 * MB for i in range(6)]
+    out = BASE + 6 * 64 * MB
+    for i in range(6):
+        p = list(good)
+        p[i] = 0
+        assert _chunk(ptrs=p, out=out) == R.ERR_INVALID_ARG, f"null input {i}"
+        p = list(good)
+        p[i] += 2
+        assert _chunk(ptrs=p, out=out) == R.ERR_INVALID_ARG, f"misaligned input {i}"
+    assert _chunk(ptrs=good, out=0) == R.ERR_INVALID_ARG
+    assert _chunk(ptrs=good, out=out + 4) == R.ERR_INVALID_ARG
+    # out overlapping an input
+    assert _chunk(ptrs=good, out=good[3] + 1024) == R.ERR_INVALID_ARG
+    # final state overlapping out, or partially overlapping the initial state
+    s0 = BASE + 8 * 64 * MB
+    assert _chunk(ptrs=good, out=out, s0=s0, sf=out + 4096) == R.ERR_INVALID_ARG
+    assert _chunk(ptrs=good, out=out, s0=s0, sf=s0 + 4096) == R.ERR_INVALID_ARG
+    # initial state misaligned
+    assert _chunk(ptrs=good, out=out, s0=s0 + 8) == R.ERR_INVALID_ARG
+
+
+def test_chunk_workspace_required_for_segments():
+    B, T, H, dk, dv = 1, 4096, 2, 64, 128
+    need = R.workspace_bytes(B, T, H, dk, dv, 0, 4)
+    assert need == B * H * 4 * (dk * dv + dk) * 4
+    good = [BASE + i * 64 * MB for i in range(6)]
+    out = BASE + 6 * 64 * MB
+    ws = BASE + 8 * 64 * MB
+    assert _chunk(B, T, H, dk, dv, segments=4, ptrs=good, out=out) == R.ERR_WORKSPACE
+    assert _chunk(B, T, H, dk, dv, segments=4, ptrs=good, out=out, ws=ws,
+                  wsb=need - 1) == R.ERR_WORKSPACE
+    # workspace overlapping an input is rejected
+    assert _chunk(B, T, H, dk, dv, segments=4, ptrs=good, out=out, ws=good[0],
+                  wsb=need) == R.ERR_INVALID_ARG
+
+
+def test_workspace_bytes_plan():
+    # one sweep when the heads fill the GPU: no workspace
+    assert R.workspace_bytes(8, 2048, 12, 64, 128) == 0
+    assert R.workspace_bytes(4, 4096, 16, 64, 128) == 0
+    # long sequence, few heads: segmented
+    ws = R.workspace_bytes(1, 65536, 16, 64, 128)
+    assert ws > 0 and ws % (16 * (64 * 128 + 64) * 4) == 0
+    # forcing one sweep
+    assert R.workspace_bytes(1, 65536, 16, 64, 128, 0, 1) == 0
+    # invalid arguments report 0
+    assert R.workspace_bytes(1, 100, 1, 48, 128) == 0
+
+
+def _decode(N=4, H=2, dk=64, dv=128, dtype=R.DTYPE_BF16, ptrs=None, state=None, out=None):
+    if ptrs is None:
+        ptrs = [BASE + i * MB for i in range(6)]
+    if state is None:
+        state = BASE + 16 * MB
+    if out is None:
+        out = BASE + 32 * MB
+    vp = ctypes.c_void_p
+    return R.lib().rodimus_ddts_decode_step(
+        N, H, dk, dv, dtype, *(vp(p) if p else None for p in ptrs),
+        vp(state) if state else None, vp(out) if out else None, None)
+
+
+def test_decode_rejects_bad_args():
+    assert _decode(N=0) == R.ERR_INVALID_ARG
+    assert _decode(H=0) == R.ERR_INVALID_ARG
+    assert _decode(dk=24) == R.ERR_UNSUPPORTED
+    assert _decode(dtype=3) == R.ERR_UNSUPPORTED
+    assert _decode(state=0) == R.ERR_INVALID_ARG
+    assert _decode(out=0) == R.ERR_INVALID_ARG
+    assert _decode(out=BASE + 16 * MB + 64) == R.ERR_INVALID_ARG      # out inside state
+    assert _decode(state=BASE + 2 * MB - 4096) == R.ERR_INVALID_ARG    # state over inputs
+    p = [BASE + i * MB for i in range(6)]
+    p[4] = 0
+    assert _decode(ptrs=p) == R.ERR_INVALID_ARG
+    p = [BASE + i * MB for i in range(6)]
+    p[2] += 4
+    assert _decode(ptrs=p) == R.ERR_INVALID_ARG
+
+
+def test_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        R.chunk_fwd(x, x, x, x, x, x)
+    with pytest.raises(ValueError):
+        R.decode_step(x[0], x[0], x[0], x[0], x[0], x[0], torch.zeros(4, 1, 16, 16))
