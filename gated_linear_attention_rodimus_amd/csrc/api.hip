@@ -26,45 +26,46 @@ Span span(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + by
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 // Pick chunk length, dv tile and segment count.  Returns false if no
-// instantiated tile shape fits the LDS for a user-fixed chunk.
+// instantiated tile shape fits the LDS.
+//  - chunk: the longest of 64/32/16 that is <= the requested one and fits;
+//  - dv tile: 64 columns (4 consumer waves) unless that leaves fewer than
+//    ~160 workgroups and halving it reaches more (then 32);
+//  - segments: when even that leaves fewer than 128 workgroups and the
+//    sequence is long, split it into pieces of >= 8 chunks (64-column tiles,
+//    so the dk-side gate work is shared by as many columns as possible).
 bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, bool f32,
                ChunkPlan *P)
 {
     const int chunks_try[3] = {64, 32, 16};
-    const int dvt_pref[3] = {64, 32, 16};
     bool found = false;
-    // a requested chunk length is an upper bound: a shorter chunk is used only
-    // where that tile shape does not fit in LDS (fp32 inputs at dk = 128)
     for (int ci = 0; ci < 3 && !found; ++ci) {
         const int C = chunks_try[ci];
         if (chunk != 0 && C > chunk) continue;
-        for (int di = 0; di < 3 && !found; ++di) {
-            const int dvt = dvt_pref[di];
-            if (dvt > dv) continue;
-            const size_t lds = chunk_lds_bytes(dk, dvt, C, f32);
-            if (lds == 0 || lds > kLdsLimit) continue;
-            P->C = C;
-            P->DVT = dvt;
-            P->lds_bytes = lds;
-            found = true;
-        }
+        const size_t lds = chunk_lds_bytes(dk, dv < 64 ? dv : 64, C, f32);
+        if (lds == 0 || lds > kLdsLimit) continue;
+        P->C = C;
+        found = true;
     }
     if (!found) return false;
     P->n_chunks = T > 0 ? (T + P->C - 1) / P->C : 0;
-    const long long cols = (long long)B * H * (dv / P->DVT);
+    const long long heads = (long long)B * H;
+    int dvt = dv < 64 ? dv : 64;
     int seg = segments;
     if (seg == 0) {
-        // one sweep per (b, h, dv tile) when that fills the GPU or the
-        // sequence is short; otherwise split the sequence into pieces of at
-        // least 8 chunks so that about kTargetBlocks workgroups run
         seg = 1;
-        if (cols < kTargetBlocks / 2 && P->n_chunks >= 32) {
-            long long want = kTargetBlocks / cols;
+        if (heads * (dv / dvt) < kTargetBlocks / 2 && P->n_chunks >= 16) {
+            long long want = kTargetBlocks / (heads * (dv / dvt));
             long long cap = P->n_chunks / 8;
             seg = (int)(want < cap ? want : cap);
             if (seg < 1) seg = 1;
         }
     }
+    if (seg == 1 && dvt > 16 && heads * (dv / dvt) < 160 &&
+        chunk_lds_bytes(dk, dvt / 2, P->C, f32) <= kLdsLimit)
+        dvt /= 2;
+    P->DVT = dvt;
+    P->lds_bytes = chunk_lds_bytes(dk, dvt, P->C, f32);
+    if (P->lds_bytes == 0 || P->lds_bytes > kLdsLimit) return false;
     if (seg > P->n_chunks) seg = P->n_chunks > 0 ? P->n_chunks : 1;
     if (seg < 1) seg = 1;
     P->chunks_per_seg = P->n_chunks > 0 ? (P->n_chunks + seg - 1) / seg : 0;
@@ -84,6 +85,8 @@ rodimus_status check_chunk_args(int B, int T, int H, int dk, int dv, int chunk, 
     if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return RODIMUS_ERR_UNSUPPORTED;
     // index arithmetic inside the kernels is 64-bit; keep the token count in int
     if ((long long)B * T > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    // per-chunk byte offsets inside the kernels are 32-bit
+    if ((long long)H * 128 * 4 * 64 > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
     return RODIMUS_OK;
 }
 

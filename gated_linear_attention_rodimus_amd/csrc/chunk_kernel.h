@@ -11,44 +11,53 @@
 // Inside a chunk of L <= C tokens (local index u), with lambda_u = -g_u*tau_u
 // and the chunk-local inclusive cumulative sum b_u = sum_{r<=u} lambda_r (per
 // column i of dk), the recurrence unrolls exactly into
-//   O   = tril(Qt Kt^T) V' + Qt' S_in            (diagonal kept)
+//   O   = tril(Qt Kt^T) V' + Qt S'                (diagonal kept)
 //   S_o = diag(exp(b_L)) S_in + Kh^T V'
 // with V' = beta_hat*v, k' = g^tau * k and
 //   Qt[u,i] = q[u,i] exp(b_u - b_m),  Kt[s,i] = k'[s,i] exp(b_m - b_s),
-//   Qt'     = Qt with S_in's rows pre-scaled by exp(b_m),
-//   Kh[s,i] = k'[s,i] exp(b_L - b_s).
+//   S'[i,:] = exp(b_m[i]) S_in[i,:],    Kh[s,i] = Kt[s,i] exp(b_L - b_m),
+// and Kh^T V' = diag(exp(b_L - b_m)) Kt^T V', so Kt serves both products.
 // b_m is the cumulative sum at the middle of the chunk: referencing the
 // exponentials there halves their range (all exponents stay within half a
 // chunk's total decay), and Qt Kt^T reproduces exp(b_u - b_s) for s <= u.
+// Cumulative sums are kept in log2 units so every exponential is one v_exp_f32;
+// alpha_hat = g^tau is folded into Kt's exponent (tau*log2 g), which leaves
+// three transcendentals per (token, dk column).
 //
 // Precision: all four products run on bf16 MFMA (v_mfma_f32_16x16x32_bf16)
 // with fp32 accumulation.  Every fp32 operand is split into NS bf16 terms
 // (x = x0 + x1 [+ x2]) and the product keeps the cross terms of total order
 // < NS: 3 MFMAs for bf16 inputs (NS = 2, ~16 mantissa bits per operand) and
-// 6 MFMAs for fp32 inputs (NS = 3, ~24 bits).  The state is carried in fp32
+// 6 MFMAs for fp32 inputs (NS = 3, ~24 bits).  The state stays in fp32
 // registers across chunks.
 //
-// Workgroup = 4 waves, owns one (b, h, dv tile of DVT columns, segment).  Per
-// chunk:
-//  1. prep: every thread owns one column (i of dk, or j of the dv tile) and a
-//     run of consecutive tokens; it loads the inputs, forms the local
-//     cumulative sum (cross-thread offsets through LDS), the gates and the
-//     scaled operands, and writes them to LDS as bf16 planes: Qt and Kt in
-//     row form [u][i], Kh^T and V'^T in column form [i][s] / [j][s] (the
-//     token dimension is the contraction for the last two products);
-//  2. each wave writes bf16 images of its state tiles (rows scaled by
-//     exp(b_m)) and computes its share of the 16x16 tiles of A^T = Kt Qt^T
-//     (upper triangle incl. diagonal), stored as register images;
-//  3. each wave computes dS = Kh^T V' for its state tiles and updates
-//     S = diag(exp(b_L)) S + dS in registers;
-//  4. each wave computes its output tiles O = A V' + Qt S' and stores fp32.
-// The MFMA operand k-slots are assigned so that a C-layout tile (rows 4g..4g+3
-// of lane group g) is directly a B operand of the next product: a 32-deep
-// k-step takes rows {4g..4g+3} of one 16-row tile and {16+4g..16+4g+3} of the
-// next, and the other operand is read from LDS with the same slot mapping.
+// Workgroup: one (b, h, dv tile of DVT columns, segment), warp-specialised.
+//  - 4 producer waves prepare chunk c+1 while the consumers compute chunk c.
+//    Each producer thread owns a pair of adjacent dk columns and a run of
+//    consecutive tokens: it forms the local cumulative sum (cross-thread
+//    offsets through LDS), the gates and Qt, Kt (row form [u][i], bf16 planes)
+//    in one of two LDS pipeline buffers, plus exp(b_m), exp(b_L) and
+//    exp(b_L - b_m) per column.
+//  - DVT/16 consumer waves; consumer w owns dv columns 16w..16w+15 of the
+//    tile for the whole sweep: its state block S[:, w] (fp32 MFMA C-layout,
+//    dk x 16), its V' columns (loaded straight into MFMA B-operand order) and
+//    its output columns.  Per chunk it builds the B operands S' from its state
+//    registers, computes its share of the 16x16 tiles of A^T = Kt Qt^T (stored
+//    as register images in LDS), then dS = diag(exp(b_L - b_m)) Kt^T V' (Kt^T
+//    through the transposing LDS read) with S = diag(exp(b_L)) S + dS, and
+//    finally its output columns O = A V' + Qt S'.
+//  Two workgroup barriers per chunk separate the phases; the consumers read
+//  the buffer the producers wrote one iteration earlier.
+// MFMA k-slots: a 32-deep k-step takes rows {4g..4g+3} of one 16-row tile and
+// {16+4g..16+4g+3} of the next (g = lane/16), so a C-layout tile (rows
+// 4g..4g+3 of lane group g) is directly a B operand of the next product; LDS
+// operands are read with the same slot mapping.
 //
-// Inputs for chunk c+1 are loaded into registers while chunk c's MFMA phases
-// run.
+// Global traffic goes through buffer resources whose size ends at the last
+// valid token of the sequence: tail-chunk loads beyond it return zero (which
+// makes those tokens inert: lambda = 0, k' = 0, v' = 0) and stores beyond it
+// are dropped, so the loop has no per-element bounds branches.  Each role
+// loads the next chunk's inputs into registers one iteration ahead.
 #pragma once
 #include "internal.h"
 
@@ -57,9 +66,8 @@
 namespace rodimus {
 namespace chunk_detail {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufFlags = 0x00020000;          // raw buffer, 32-bit data format (gfx9)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -72,6 +80,48 @@ __device__ __forceinline__ float in_to_f32(float x) { return x; }
 template <typename TIn> struct InRaw;
 template <> struct InRaw<__bf16> { typedef u16 type; };
 template <> struct InRaw<float> { typedef float type; };
+
+__device__ __forceinline__ u16 buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, u16) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, float) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Two adjacent elements of a per-token input: one 32-bit word for bf16, two
+// for fp32.
+template <typename TIn> struct Pair;
+template <> struct Pair<__bf16> {
+    typedef unsigned type;
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x << 16); }
+    static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x & 0xffff0000u); }
+};
+template <> struct Pair<float> {
+    typedef unsigned type __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x[0]); }
+    static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x[1]); }
+};
+
+// Buffer resource over [p, p + bytes); bytes is clamped to 31 bits.  The
+// arguments are wave-uniform; readfirstlane states that to the compiler so the
+// descriptor lives in SGPRs (a descriptor it cannot prove uniform turns every
+// load into a readfirstlane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, long long bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+    const unsigned long long a = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    void *base = (void *)(((unsigned long long)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, n, kBufFlags);
+}
 
 // Split x into NS bf16 terms, x ~= p[0] + p[1] (+ p[2]); each residual is exact in fp32.
 template <int NS>
@@ -96,7 +146,8 @@ __device__ __forceinline__ bf16x4 zero4() {
     return z;
 }
 
-// acc += sum over split-term pairs (a, b) with a + b < NS of A[a] * B[b].
+// acc += sum over split-term pairs (a, b) with a + b < NS of A[a] * B[b]
+// (smallest terms first).
 template <int NS>
 __device__ __forceinline__ f32x4 mma_split(const bf16x8 *A, const bf16x8 *Bv, f32x4 acc) {
     if constexpr (NS == 3) {
@@ -124,50 +175,81 @@ struct Args {
     int remap;                   // XCD-aware block mapping on/off
 };
 
-// LDS layout (bytes), shared by the host-side size query.
-template <int DK, int DVT, int C, int NS>
-struct Lds {
-    static constexpr int NU = C / 16, NI = DK / 16, NJ = DVT / 16;
-    static constexpr int NA = NU * (NU + 1) / 2;
-    static constexpr int NG = kThreads / DK;          // token groups for dk columns
-    static constexpr int RS = DK + 8;                 // row-form stride (bf16)
-    static constexpr int CS = C + 8;                  // column-form stride (bf16)
-    static constexpr size_t q_off = 0;
-    static constexpr size_t k_off = q_off + (size_t)NS * C * RS * 2;
-    static constexpr size_t kh_off = k_off + (size_t)NS * C * RS * 2;
-    static constexpr size_t v_off = kh_off + (size_t)NS * DK * CS * 2;
-    static constexpr size_t a_off = v_off + (size_t)NS * DVT * CS * 2;
-    static constexpr size_t s_off = a_off + (size_t)NA * NS * 64 * 4 * 2;
-    static constexpr size_t tot_off = s_off + (size_t)NI * NJ * NS * 64 * 4 * 2;
-    static constexpr size_t gam_off = tot_off + (size_t)NG * DK * 4;
-    static constexpr size_t em_off = gam_off + (size_t)DK * 4;
-    static constexpr size_t bytes = em_off + (size_t)DK * 4;
+// log2 of alpha_hat = g^tau: tau * log2(g), and exactly 0 when tau == 0 (g^0 = 1,
+// also at g = 0 where log2(g) = -inf).
+__device__ __forceinline__ float log2_gate_pow(float g, float tau) {
+    return tau == 0.f ? 0.f : tau * __builtin_amdgcn_logf(g);
+}
+
+// Transposed LDS read of a 16-bit operand (gfx950 ds_read_b64_tr_b16).  Within
+// each 16-lane group, lane m passes the address of 4 consecutive 16-bit values
+// (row m/4, columns 4*(m%4)..+3 of a 4 x 16 block); lane i receives column i
+// of the block, rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(const_cast<__bf16 *>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Compile-time shape of one instantiation, and its LDS layout (bytes).
+template <int DK, int DVT, int C, int NS_>
+struct Cfg {
+    static constexpr int NS = NS_;
+    static constexpr int NP = 4;                              // producer waves
+    static constexpr int NJ = DVT / 16;                       // consumer waves
+    static constexpr int NW = NP + NJ;
+    static constexpr int NT = 64 * NW;                        // threads
+    static constexpr int NU = C / 16, NI = DK / 16;
+    static constexpr int NA = NU * (NU + 1) / 2;              // A^T tiles (upper triangle)
+    static constexpr int PP = DK / 2;                         // dk column pairs
+    static constexpr int NG0 = 64 * NP / PP;                  // token groups per column pair
+    static constexpr int NG = NG0 < C ? NG0 : C;              // groups actually used
+    static constexpr int TPG = C / NG;                        // tokens per group
+    // raw-input register sets of the producers (chunks in flight); a second
+    // set costs more in register spills than it gains in latency hiding
+    static constexpr int PF = 1;
+    static constexpr int KSI = (DK + 31) / 32;                // k-steps over dk
+    static constexpr int KSC = (C + 31) / 32;                 // k-steps over tokens
+    static constexpr int RS = DK + 4;                         // row stride (bf16)
+    static constexpr int MID = C / 2 - 1;                     // reference token b_m
+    // one pipeline buffer: Qt and Kt planes, exp(b_m), exp(b_L), exp(b_L - b_m)
+    static constexpr size_t bq_off = 0;
+    static constexpr size_t bk_off = bq_off + (size_t)NS * C * RS * 2;
+    static constexpr size_t bem_off = bk_off + (size_t)NS * C * RS * 2;
+    static constexpr size_t bgam_off = bem_off + (size_t)DK * 4;
+    static constexpr size_t bgm_off = bgam_off + (size_t)DK * 4;
+    static constexpr size_t buf_bytes = (bgm_off + (size_t)DK * 4 + 15) / 16 * 16;
+    static constexpr size_t a_off = 2 * buf_bytes;
+    static constexpr size_t tot_off = a_off + (size_t)NA * NS * 64 * 4 * 2;
+    static constexpr size_t mid_off = tot_off + (size_t)NG * DK * 4;
+    static constexpr size_t bytes = mid_off + (size_t)DK * 4;
+    static_assert(NG >= 1 && TPG * NG == C, "token groups");
+    static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
 
 template <int DK, int DVT, int C, typename TIn>
-__global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Args a)
+__global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(Args a)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    typedef Lds<DK, DVT, C, NS> L;
+    typedef Cfg<DK, DVT, C, NS> L;
     typedef typename InRaw<TIn>::type Raw;
-    constexpr int NU = L::NU, NI = L::NI, NJ = L::NJ, NA = L::NA;
-    constexpr int RS = L::RS, CS = L::CS;
-    // column-owner layout for the dk tensors and for the dv tile
-    constexpr int NG = kThreads / DK, TPG = C / NG;
-    constexpr int NGV = kThreads / DVT, TPGV = C / NGV;
-    static_assert(TPG >= 1 && TPGV >= 1, "chunk too small for the tile");
-    constexpr int SPW = (NI * NJ + kWaves - 1) / kWaves;      // state tiles per wave
+    typedef Pair<TIn> PR;
+    typedef typename PR::type Raw2;
+    constexpr int NU = L::NU, NI = L::NI, NJ = L::NJ, NA = L::NA, NP = L::NP, PP = L::PP;
+    constexpr int NG = L::NG, TPG = L::TPG, KSI = L::KSI, KSC = L::KSC, PF = L::PF;
+    constexpr int RS = L::RS, MID = L::MID;
+    constexpr int esz = sizeof(Raw);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __bf16 *sQ = (__bf16 *)(smem + L::q_off);
-    __bf16 *sK = (__bf16 *)(smem + L::k_off);
-    __bf16 *sKh = (__bf16 *)(smem + L::kh_off);
-    __bf16 *sV = (__bf16 *)(smem + L::v_off);
     __bf16 *sA = (__bf16 *)(smem + L::a_off);
-    __bf16 *sS = (__bf16 *)(smem + L::s_off);
     float *sTot = (float *)(smem + L::tot_off);
-    float *sGam = (float *)(smem + L::gam_off);
-    float *sEm = (float *)(smem + L::em_off);
+    float *sMid = (float *)(smem + L::mid_off);
+    auto bQ = [&](int buf) { return (__bf16 *)(smem + buf * L::buf_bytes + L::bq_off); };
+    auto bK = [&](int buf) { return (__bf16 *)(smem + buf * L::buf_bytes + L::bk_off); };
+    auto bEm = [&](int buf) { return (float *)(smem + buf * L::buf_bytes + L::bem_off); };
+    auto bGam = [&](int buf) { return (float *)(smem + buf * L::buf_bytes + L::bgam_off); };
+    auto bGm = [&](int buf) { return (float *)(smem + buf * L::buf_bytes + L::bgm_off); };
 
     // ---- block -> (b, h, dv tile, segment); XCD-aware: consecutive logical ids
     // (the dv tiles of one head first) land on the same XCD, which shares L2.
@@ -179,187 +261,168 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Args a)
     const int seg = rest % a.n_seg;
     const int bh = rest / a.n_seg;
     const int b = bh / a.H, h = bh % a.H;
-    const int j0 = jt * DVT;
     const int c_begin = seg * a.chunks_per_seg;
     const int c_end = min(a.n_chunks, c_begin + a.chunks_per_seg);
     const bool outputs = a.mode == 0;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lc = lane & 15, lg = lane >> 4;          // MFMA lane column / group
-    const int ci = tid % DK, cgp = tid / DK;           // dk column owner
-    const int cj = tid % DVT, cgv = tid / DVT;         // dv column owner
+    const bool producer = wave < NP;
+    const int cw = wave - NP;                          // consumer index (dv block)
+    const int jcol = jt * DVT + (producer ? 0 : cw) * 16;
+    const int cp = tid % PP, cgp = tid / PP;           // producer: dk column pair owner
+    const int c0 = 2 * cp;                             // its columns c0, c0 + 1
+    const bool prep = producer && cgp < NG;
 
-    const Raw *gq = (const Raw *)a.q, *gk = (const Raw *)a.k, *gg = (const Raw *)a.g;
-    const Raw *gt = (const Raw *)a.tau, *gv = (const Raw *)a.v, *gb = (const Raw *)a.beta;
+    const long long T = a.T, H = a.H, dv = a.dv;
+    const long long row_k = H * DK, row_v = H * dv;    // elements between tokens
+    const long long head0 = (long long)b * T * H + h;
+    const Raw *gq = (const Raw *)a.q + head0 * DK;
+    const Raw *gk = (const Raw *)a.k + head0 * DK;
+    const Raw *gg = (const Raw *)a.g + head0 * DK;
+    const Raw *gt = (const Raw *)a.tau + head0 * DK;
+    const Raw *gv = (const Raw *)a.v + head0 * dv + jcol;
+    const Raw *gb = (const Raw *)a.beta + head0 * dv + jcol;
+    float *go = a.out ? a.out + head0 * dv + jcol : nullptr;
 
-    // ---- state tiles owned by this wave, fp32 C-layout: S[slot][r] holds
-    // row I*16 + 4*lg + r, column J*16 + lc of the dv tile.
-    float S[SPW][4];
+    // byte offsets of this thread's elements inside one chunk
+    const unsigned off_k = (unsigned)(((long long)cgp * TPG * row_k + c0) * esz);
+    const unsigned off_v = (unsigned)(((long long)4 * lg * row_v + lc) * esz);
+    const unsigned step_k = (unsigned)(row_k * esz), step_v = (unsigned)(row_v * esz);
+
+    // ---- consumer state block: S[I][r] = row I*16 + 4*lg + r, column jcol + lc
+    float S[NI][4];
     {
         const float *sin = a.s_in ? a.s_in + bh * a.s_in_bh + seg * a.s_in_seg : nullptr;
 #pragma unroll
-        for (int slot = 0; slot < SPW; ++slot) {
-            const int idx = slot * kWaves + wave;
-            const int I = idx / NJ, J = idx % NJ;
+        for (int I = 0; I < NI; ++I)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = 0.f;
-                if (idx < NI * NJ && sin)
-                    x = sin[(size_t)(I * 16 + 4 * lg + r) * a.dv + j0 + J * 16 + lc];
-                S[slot][r] = x;
-            }
-        }
+            for (int r = 0; r < 4; ++r)
+                S[I][r] = (sin && !producer) ? sin[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] : 0.f;
     }
-    float gam_acc = 1.f;                                // product of chunk decays (mode 1)
+    float gam_acc0 = 1.f, gam_acc1 = 1.f;               // products of chunk decays (mode 1)
 
-    // ---- raw input registers for one chunk
-    Raw rq[TPG], rk[TPG], rg[TPG], rt[TPG], rv[TPGV], rb[TPGV];
-    auto load_chunk = [&](int ch) {
-        const int t0 = ch * C;
+    // ---- raw inputs in registers: producers hold PF chunks of q, k, g, tau
+    // (a dk column pair, TPG consecutive tokens); consumers hold one chunk of
+    // their v, beta_hat columns in MFMA B-operand order (k = tokens).
+    Raw2 rq[PF][TPG], rk[PF][TPG], rg[PF][TPG], rt[PF][TPG];
+    Raw rv[KSC][8], rb[KSC][8];
+    auto load_dk = [&](int ch, auto rsel) {
+        constexpr int R = decltype(rsel)::value;
+        const long long t0 = (long long)ch * C;
+        const long long base = t0 * row_k;
+        const long long lim = ((T - t0) * H - h) * DK * esz;
+        const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
+        const __amdgpu_buffer_rsrc_t Rg = make_rsrc(gg + base, lim);
+        const __amdgpu_buffer_rsrc_t Rt = make_rsrc(gt + base, lim);
+        const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, outputs ? lim : 0);
 #pragma unroll
         for (int m = 0; m < TPG; ++m) {
-            const int tok = t0 + cgp * TPG + m;
-            const bool ok = tok < a.T;
-            const size_t idx = (((size_t)b * a.T + (ok ? tok : 0)) * a.H + h) * DK + ci;
-            rq[m] = (ok && outputs) ? gq[idx] : Raw(0);
-            rk[m] = ok ? gk[idx] : Raw(0);
-            rg[m] = ok ? gg[idx] : Raw(0);
-            rt[m] = ok ? gt[idx] : Raw(0);
-        }
-#pragma unroll
-        for (int m = 0; m < TPGV; ++m) {
-            const int tok = t0 + cgv * TPGV + m;
-            const bool ok = tok < a.T;
-            const size_t idx = (((size_t)b * a.T + (ok ? tok : 0)) * a.H + h) * a.dv + j0 + cj;
-            rv[m] = ok ? gv[idx] : Raw(0);
-            rb[m] = ok ? gb[idx] : Raw(0);
+            const unsigned o = off_k + m * step_k;
+            rq[R][m] = PR::load(Rq, o);
+            rk[R][m] = PR::load(Rk, o);
+            rg[R][m] = PR::load(Rg, o);
+            rt[R][m] = PR::load(Rt, o);
         }
     };
-
-    if (c_begin < c_end) load_chunk(c_begin);
-
-    for (int ch = c_begin; ch < c_end; ++ch) {
-        const int t0 = ch * C;
-
-        // ================= 1. prep: cumulative decay, gates, operands -> LDS
-        float cum[TPG];
-        {
-            float run = 0.f;
+    auto load_v = [&](int ch) {
+        const long long t0 = (long long)ch * C;
+        const long long base = t0 * row_v;
+        const long long lim = ((T - t0) * H - h) * dv * esz - (long long)jcol * esz;
+        const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lim);
+        const __amdgpu_buffer_rsrc_t Rb = make_rsrc(gb + base, lim);
 #pragma unroll
-            for (int m = 0; m < TPG; ++m) {
-                run += -(in_to_f32(rg[m]) * in_to_f32(rt[m]));
-                cum[m] = run;
-            }
-            sTot[cgp * DK + ci] = run;
-        }
-        __syncthreads();
-        float off = 0.f, bm = 0.f, bL = 0.f;
+        for (int p = 0; p < KSC; ++p)
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const float x = sTot[gi * DK + ci];
-            if (gi < cgp) off += x;
-            if (gi < NG / 2) bm += x;
-            bL += x;
-        }
-        {
-            __bf16 kh_pl[NS][TPG];
-#pragma unroll
-            for (int m = 0; m < TPG; ++m) {
-                const int u = cgp * TPG + m;
-                const float bu = off + cum[m];
-                const float gv_ = in_to_f32(rg[m]), tv_ = in_to_f32(rt[m]);
-                const float kv_ = in_to_f32(rk[m]);
-                // log2 of alpha_hat = tau*log2(g), with pow semantics at g = 0
-                const float la = gv_ > 0.f ? tv_ * __builtin_amdgcn_logf(gv_)
-                                           : (tv_ == 0.f ? 0.f : -INFINITY);
-                __bf16 p[NS];
-                if (outputs) {
-                    const float qt = in_to_f32(rq[m]) * __builtin_amdgcn_exp2f((bu - bm) * kLog2e);
-                    split<NS>(qt, p);
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) sQ[(n * C + u) * RS + ci] = p[n];
-                    const float kt = kv_ * __builtin_amdgcn_exp2f(la + (bm - bu) * kLog2e);
-                    split<NS>(kt, p);
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) sK[(n * C + u) * RS + ci] = p[n];
+            for (int e = 0; e < 8; ++e) {
+                const int u = p * 32 + (e < 4 ? e : 12 + e);            // + 4*lg via off_v
+                if (u < C) {
+                    const unsigned o = off_v + u * step_v;
+                    rv[p][e] = buf_load(Rv, o, Raw());
+                    rb[p][e] = buf_load(Rb, o, Raw());
+                } else {
+                    rv[p][e] = Raw(0);
+                    rb[p][e] = Raw(0);
                 }
-                const float kh = kv_ * __builtin_amdgcn_exp2f(la + (bL - bu) * kLog2e);
-                split<NS>(kh, p);
-#pragma unroll
-                for (int n = 0; n < NS; ++n) kh_pl[n][m] = p[n];
             }
-#pragma unroll
-            for (int n = 0; n < NS; ++n) {
-                __bf16 *dst = sKh + (n * DK + ci) * CS + cgp * TPG;
-#pragma unroll
-                for (int m = 0; m < TPG; ++m) dst[m] = kh_pl[n][m];
-            }
-        }
-        if (cgp == 0) {
-            sGam[ci] = __builtin_amdgcn_exp2f(bL * kLog2e);
-            sEm[ci] = __builtin_amdgcn_exp2f(bm * kLog2e);
-        }
-        {
-            __bf16 v_pl[NS][TPGV];
-#pragma unroll
-            for (int m = 0; m < TPGV; ++m) {
-                __bf16 p[NS];
-                split<NS>(in_to_f32(rb[m]) * in_to_f32(rv[m]), p);
-#pragma unroll
-                for (int n = 0; n < NS; ++n) v_pl[n][m] = p[n];
-            }
-#pragma unroll
-            for (int n = 0; n < NS; ++n) {
-                __bf16 *dst = sV + (n * DVT + cj) * CS + cgv * TPGV;
-#pragma unroll
-                for (int m = 0; m < TPGV; ++m) dst[m] = v_pl[n][m];
-            }
-        }
-        __syncthreads();
+    };
+    typedef std::integral_constant<int, 0> R0;
+    typedef std::integral_constant<int, PF - 1> R1;
 
-        // prefetch the next chunk's inputs while the MFMA phases run
-        if (ch + 1 < c_end) load_chunk(ch + 1);
+    if (c_begin < c_end) {
+        if (prep) {
+            load_dk(c_begin, R0());
+            if (PF == 2 && c_begin + 1 < c_end) load_dk(c_begin + 1, R1());
+        }
+        if (!producer) load_v(c_begin);
+    }
 
-        // ================= 2. state images (rows scaled by exp(b_m)) and A^T tiles
-        if (outputs) {
+    // Pipeline: in iteration it the producers prepare chunk it (LDS buffer
+    // it & 1, raw registers (it - c_begin) % PF) while the consumers compute
+    // chunk it - 1 (LDS buffer (it - 1) & 1).
+    auto body = [&](int it, auto rsel) {
+        constexpr int R = decltype(rsel)::value;
+        const bool pwork = it < c_end;
+        const bool cwork = it > c_begin;
+        const int pb = it & 1, cb = (it - 1) & 1;
+
+        // ================= phase 1
+        float cum0[TPG], cum1[TPG];
+        bf16x8 sB[KSI][NS];
+        if (prep && pwork) {
+            // local cumulative decay of both columns, in log2 units
+            float run0 = 0.f, run1 = 0.f;
 #pragma unroll
-            for (int slot = 0; slot < SPW; ++slot) {
-                const int idx = slot * kWaves + wave;
-                if (idx < NI * NJ) {
-                    const int I = idx / NJ;
-                    __bf16 pl[NS][4];
+            for (int m = 0; m < TPG; ++m) {
+                run0 = __builtin_fmaf(PR::lo(rg[R][m]) * PR::lo(rt[R][m]), -kLog2e, run0);
+                run1 = __builtin_fmaf(PR::hi(rg[R][m]) * PR::hi(rt[R][m]), -kLog2e, run1);
+                cum0[m] = run0;
+                cum1[m] = run1;
+            }
+            *(float2 *)(sTot + cgp * DK + c0) = make_float2(run0, run1);
+            if (MID / TPG == cgp)
+                *(float2 *)(sMid + c0) = make_float2(cum0[MID % TPG], cum1[MID % TPG]);
+        }
+        if (!producer && cwork && outputs) {
+            // B operands S' = diag(exp(b_m)) S_in (k = dk rows)
+            const float *em = bEm(cb);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        __bf16 p[NS];
-                        split<NS>(S[slot][r] * sEm[I * 16 + 4 * lg + r], p);
+            for (int ks = 0; ks < KSI; ++ks) {
+                const int I0 = 2 * ks, I1 = 2 * ks + 1;
+                const f32x4 e0 = *(const f32x4 *)(em + I0 * 16 + 4 * lg);
+                f32x4 e1 = {0.f, 0.f, 0.f, 0.f};
+                if (I1 < NI) e1 = *(const f32x4 *)(em + I1 * 16 + 4 * lg);
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) pl[n][r] = p[n];
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    __bf16 t0_[NS], t1_[NS];
+                    split<NS>(S[I0][r] * e0[r], t0_);
+                    split<NS>(I1 < NI ? S[I1 < NI ? I1 : 0][r] * e1[r] : 0.f, t1_);
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
-                        bf16x4 w;
-                        w[0] = pl[n][0]; w[1] = pl[n][1]; w[2] = pl[n][2]; w[3] = pl[n][3];
-                        *(bf16x4 *)(sS + ((idx * NS + n) * 64 + lane) * 4) = w;
+                        sB[ks][n][r] = t0_[n];
+                        sB[ks][n][4 + r] = t1_[n];
                     }
                 }
             }
-            // A^T tile (Sb, Ub), Sb <= Ub: rows s of Kt, columns u of Qt, k = i
+            // A^T tiles (Sb, Ub), Sb <= Ub: rows s of Kt, columns u of Qt, k = i
+            const __bf16 *qb = bQ(cb), *kb = bK(cb);
 #pragma unroll
             for (int Ub = 0; Ub < NU; ++Ub) {
 #pragma unroll
                 for (int Sb = 0; Sb <= Ub; ++Sb) {
                     const int tix = Ub * (Ub + 1) / 2 + Sb;
-                    if (tix % kWaves != wave) continue;
+                    if (tix % NJ != cw) continue;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < (DK + 31) / 32; ++ks) {
+                    for (int ks = 0; ks < KSI; ++ks) {
                         const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
                         bf16x8 A[NS], Bv[NS];
 #pragma unroll
                         for (int n = 0; n < NS; ++n) {
-                            const __bf16 *kr = sK + (n * C + Sb * 16 + lc) * RS;
-                            const __bf16 *qr = sQ + (n * C + Ub * 16 + lc) * RS;
+                            const __bf16 *kr = kb + (n * C + Sb * 16 + lc) * RS;
+                            const __bf16 *qr = qb + (n * C + Ub * 16 + lc) * RS;
                             const bf16x4 klo = *(const bf16x4 *)(kr + i_lo);
                             const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
                             const bf16x4 khi = i_hi < DK ? *(const bf16x4 *)(kr + i_hi) : zero4();
@@ -388,121 +451,183 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Args a)
                 }
             }
         }
+        __syncthreads();                                   // barrier A
 
-        // ================= 3. dS = Kh^T V' and S = diag(exp(b_L)) S + dS
+        // ================= phase 2
+        if (producer) {
+            if (prep && pwork) {
+                float off0 = 0.f, off1 = 0.f, bm0 = 0.f, bm1 = 0.f, bL0 = 0.f, bL1 = 0.f;
 #pragma unroll
-        for (int slot = 0; slot < SPW; ++slot) {
-            const int idx = slot * kWaves + wave;
-            if (idx < NI * NJ) {
-                const int I = idx / NJ, J = idx % NJ;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int gi = 0; gi < NG; ++gi) {
+                    const float2 x = *(const float2 *)(sTot + gi * DK + c0);
+                    if (gi < cgp) { off0 += x.x; off1 += x.y; }
+                    if (gi < MID / TPG) { bm0 += x.x; bm1 += x.y; }
+                    bL0 += x.x; bL1 += x.y;
+                }
+                const float2 mid = *(const float2 *)(sMid + c0);
+                bm0 += mid.x; bm1 += mid.y;
+                const float sh0 = off0 - bm0, sh1 = off1 - bm1;
+                __bf16 *qb = bQ(pb), *kb = bK(pb);
 #pragma unroll
-                for (int ks = 0; ks < (C + 31) / 32; ++ks) {
-                    const int s_lo = ks * 32 + 4 * lg, s_hi = s_lo + 16;
-                    bf16x8 A[NS], Bv[NS];
+                for (int m = 0; m < TPG; ++m) {
+                    const int u = cgp * TPG + m;
+                    const float d0 = cum0[m] + sh0, d1 = cum1[m] + sh1;          // b_u - b_m
+                    // log2 of alpha_hat = tau * log2(g) (0 when tau = 0, also at g = 0)
+                    const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
+                    const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
+                    __bf16 p0[NS], p1[NS];
+                    split<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0), p0);
+                    split<NS>(PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), p1);
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
-                        const __bf16 *kr = sKh + (n * DK + I * 16 + lc) * CS;
-                        const __bf16 *vr = sV + (n * DVT + J * 16 + lc) * CS;
-                        const bf16x4 klo = *(const bf16x4 *)(kr + s_lo);
-                        const bf16x4 vlo = *(const bf16x4 *)(vr + s_lo);
-                        const bf16x4 khi = s_hi < C ? *(const bf16x4 *)(kr + s_hi) : zero4();
-                        const bf16x4 vhi = s_hi < C ? *(const bf16x4 *)(vr + s_hi) : zero4();
-                        A[n] = cat(klo, khi);
-                        Bv[n] = cat(vlo, vhi);
+                        __bf16 pr[2] = {p0[n], p1[n]};
+                        *(unsigned *)(kb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
                     }
-                    acc = mma_split<NS>(A, Bv, acc);
+                    if (outputs) {
+                        split<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0), p0);
+                        split<NS>(PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), p1);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            __bf16 pr[2] = {p0[n], p1[n]};
+                            *(unsigned *)(qb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
+                        }
+                    }
+                }
+                if (cgp == 0) {
+                    const float g0 = __builtin_amdgcn_exp2f(bL0), g1 = __builtin_amdgcn_exp2f(bL1);
+                    *(float2 *)(bGam(pb) + c0) = make_float2(g0, g1);
+                    *(float2 *)(bEm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bm0),
+                                                            __builtin_amdgcn_exp2f(bm1));
+                    *(float2 *)(bGm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bL0 - bm0),
+                                                            __builtin_amdgcn_exp2f(bL1 - bm1));
+                    gam_acc0 *= g0;
+                    gam_acc1 *= g1;
+                }
+            }
+            if (prep && it + PF < c_end) load_dk(it + PF, rsel);
+        } else if (cwork) {
+            const long long t0 = (long long)(it - 1) * C;
+            // V' = beta_hat * v of this wave's columns, as split B operands (k = tokens)
+            bf16x8 vB[KSC][NS];
+#pragma unroll
+            for (int p = 0; p < KSC; ++p) {
+                __bf16 pl[NS][8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 t[NS];
+                    split<NS>(in_to_f32(rb[p][e]) * in_to_f32(rv[p][e]), t);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) pl[n][e] = t[n];
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[slot][r] = sGam[I * 16 + 4 * lg + r] * S[slot][r] + acc[r];
+                for (int n = 0; n < NS; ++n)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vB[p][n][e] = pl[n][e];
             }
-        }
-        if (!outputs) {
-            gam_acc *= sGam[ci];
-            __syncthreads();           // LDS is rewritten by the next chunk's prep
-            continue;
-        }
-        __syncthreads();
+            if (it < c_end) load_v(it);                     // next chunk's v, beta_hat
 
-        // ================= 4. O = A V' + Qt S'  (output tiles (Ub, J))
+            // dS = diag(exp(b_L - b_m)) Kt^T V' and S = diag(exp(b_L)) S + dS;
+            // Kt^T is read with the transposing LDS read (k = tokens)
+            const __bf16 *kb = bK(cb);
+            const float *gam = bGam(cb), *gmv = bGm(cb);
+            const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
 #pragma unroll
-        for (int ot = 0; ot < NU * NJ; ++ot) {
-            if (ot % kWaves != wave) continue;
-            const int Ub = ot / NJ, J = ot % NJ;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            // intra-chunk: k = s over token blocks 0..Ub, two 16-blocks per step
+            for (int I = 0; I < NI; ++I) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p <= Ub / 2; ++p) {
-                const int S0 = 2 * p, S1 = 2 * p + 1;
-                const int s_lo = p * 32 + 4 * lg, s_hi = s_lo + 16;
-                bf16x8 A[NS], Bv[NS];
+                for (int ks = 0; ks < KSC; ++ks) {
+                    const int s_lo = ks * 32 + trow, s_hi = s_lo + 16;
+                    bf16x8 A[NS];
 #pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const int t0x = Ub * (Ub + 1) / 2 + S0;
-                    const bf16x4 alo = *(const bf16x4 *)(sA + ((t0x * NS + n) * 64 + lane) * 4);
-                    const bf16x4 ahi = S1 <= Ub
-                        ? *(const bf16x4 *)(sA + (((t0x + 1) * NS + n) * 64 + lane) * 4) : zero4();
-                    const __bf16 *vr = sV + (n * DVT + J * 16 + lc) * CS;
-                    const bf16x4 vlo = *(const bf16x4 *)(vr + s_lo);
-                    const bf16x4 vhi = (S1 <= Ub) ? *(const bf16x4 *)(vr + s_hi) : zero4();
-                    A[n] = cat(alo, ahi);
-                    Bv[n] = cat(vlo, vhi);
+                    for (int n = 0; n < NS; ++n) {
+                        const __bf16 *base = kb + n * C * RS + I * 16 + tcol;
+                        const bf16x4 klo = lds_read_tr(base + s_lo * RS);
+                        const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
+                        A[n] = cat(klo, khi);
+                    }
+                    acc = mma_split<NS>(A, vB[ks], acc);
                 }
-                acc = mma_split<NS>(A, Bv, acc);
+                const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
+                const f32x4 g1 = *(const f32x4 *)(gmv + I * 16 + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[r], g0[r] * S[I][r]);
             }
-            // inter-chunk: k = i, A = Qt rows, B = state images of tiles (2ks, J), (2ks+1, J)
+
+            if (outputs) {
+                // O = A V' + Qt S' for this wave's columns
+                const long long lim = ((T - t0) * H - h) * dv * 4 - (long long)jcol * 4;
+                const __amdgpu_buffer_rsrc_t Ro = make_rsrc(go + t0 * row_v, lim);
+                const __bf16 *qb = bQ(cb);
 #pragma unroll
-            for (int ks = 0; ks < (DK + 31) / 32; ++ks) {
-                const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
-                const int I0 = 2 * ks, I1 = 2 * ks + 1;
-                bf16x8 A[NS], Bv[NS];
+                for (int Ub = 0; Ub < NU; ++Ub) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    // intra-chunk: k = s over token blocks 0..Ub, two 16-blocks per step
 #pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const __bf16 *qr = sQ + (n * C + Ub * 16 + lc) * RS;
-                    const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
-                    const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
-                    const bf16x4 slo = *(const bf16x4 *)(sS + (((I0 * NJ + J) * NS + n) * 64 + lane) * 4);
-                    const bf16x4 shi = I1 < NI
-                        ? *(const bf16x4 *)(sS + (((I1 * NJ + J) * NS + n) * 64 + lane) * 4) : zero4();
-                    A[n] = cat(qlo, qhi);
-                    Bv[n] = cat(slo, shi);
+                    for (int p = 0; p <= Ub / 2; ++p) {
+                        const int S1 = 2 * p + 1;
+                        const int t0x = Ub * (Ub + 1) / 2 + 2 * p;
+                        bf16x8 A[NS], Bv[NS];
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const bf16x4 alo = *(const bf16x4 *)(sA + ((t0x * NS + n) * 64 + lane) * 4);
+                            const bf16x4 ahi = S1 <= Ub
+                                ? *(const bf16x4 *)(sA + (((t0x + 1) * NS + n) * 64 + lane) * 4) : zero4();
+                            A[n] = cat(alo, ahi);
+                            Bv[n] = vB[p][n];
+                            if (S1 > Ub)           // keep only the first 16 tokens of this k-step
+                                for (int e = 4; e < 8; ++e) Bv[n][e] = (__bf16)0.f;
+                        }
+                        acc = mma_split<NS>(A, Bv, acc);
+                    }
+                    // inter-chunk: k = i, A = Qt rows, B = S'
+#pragma unroll
+                    for (int ks = 0; ks < KSI; ++ks) {
+                        const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
+                        bf16x8 A[NS];
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const __bf16 *qr = qb + (n * C + Ub * 16 + lc) * RS;
+                            const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
+                            const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
+                            A[n] = cat(qlo, qhi);
+                        }
+                        acc = mma_split<NS>(A, sB[ks], acc);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const unsigned o = (unsigned)((((long long)(Ub * 16 + 4 * lg + r)) * row_v + lc) * 4);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), Ro, o, 0, 0);
+                    }
                 }
-                acc = mma_split<NS>(A, Bv, acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = t0 + Ub * 16 + 4 * lg + r;
-                if (tok < a.T)
-                    a.out[(((size_t)b * a.T + tok) * a.H + h) * a.dv + j0 + J * 16 + lc] = acc[r];
             }
         }
-        __syncthreads();               // LDS is rewritten by the next chunk's prep
+        __syncthreads();                                   // barrier B
+    };
+
+    for (int it = c_begin; it <= c_end; it += PF) {
+        body(it, R0());
+        if (PF == 2 && it + 1 <= c_end) body(it + 1, R1());
     }
 
     // ---- state out
-    if (a.s_out && (!a.s_out_last_only || seg == a.n_seg - 1)) {
+    if (!producer && a.s_out && (!a.s_out_last_only || seg == a.n_seg - 1)) {
         float *so = a.s_out + bh * a.s_out_bh + seg * a.s_out_seg;
 #pragma unroll
-        for (int slot = 0; slot < SPW; ++slot) {
-            const int idx = slot * kWaves + wave;
-            if (idx < NI * NJ) {
-                const int I = idx / NJ, J = idx % NJ;
+        for (int I = 0; I < NI; ++I)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    so[(size_t)(I * 16 + 4 * lg + r) * a.dv + j0 + J * 16 + lc] = S[slot][r];
-            }
-        }
+            for (int r = 0; r < 4; ++r)
+                so[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] = S[I][r];
     }
-    if (!outputs && a.gam_out && jt == 0 && cgp == 0)
-        a.gam_out[((size_t)bh * a.n_seg + seg) * DK + ci] = gam_acc;
+    if (!outputs && a.gam_out && jt == 0 && prep && cgp == 0)
+        *(float2 *)(a.gam_out + ((size_t)bh * a.n_seg + seg) * DK + c0) = make_float2(gam_acc0, gam_acc1);
 }
 
 template <int DK, int DVT, int C, typename TIn>
 hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    const size_t lds = Lds<DK, DVT, C, NS>::bytes;
+    typedef Cfg<DK, DVT, C, NS> L;
+    const size_t lds = L::bytes;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DK, DVT, C, TIn>,
@@ -524,40 +649,33 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
     a.gam_out = Lc.gam_out;
     const long long blocks = (long long)Lc.B * Lc.H * Lc.n_seg * a.n_jt;
     a.remap = (blocks % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn>), dim3((unsigned)blocks), dim3(kThreads),
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn>), dim3((unsigned)blocks), dim3(L::NT),
                        lds, stream, a);
     return hipGetLastError();
 }
 
 // Instantiates every (DVT, C) tile shape for one dk and defines its size
 // query and launcher.
+#define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC)                                            \
+    if (dvt == XV && C == XC)                                                         \
+        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3>::bytes : chunk_detail::Cfg<XK, XV, XC, 2>::bytes;
+#define RODIMUS_CHUNK_CASE_LAUNCH(XK, XV, XC)                                         \
+    if (Lc.DVT == XV && Lc.C == XC)                                                   \
+        return Lc.f32_inputs ? chunk_detail::launch_t<XK, XV, XC, float>(Lc, stream)  \
+                             : chunk_detail::launch_t<XK, XV, XC, __bf16>(Lc, stream);
+#define RODIMUS_CHUNK_SHAPES(X, XK)                                                   \
+    X(XK, 16, 16) X(XK, 16, 32) X(XK, 16, 64)                                         \
+    X(XK, 32, 16) X(XK, 32, 32) X(XK, 32, 64)                                         \
+    X(XK, 64, 16) X(XK, 64, 32) X(XK, 64, 64)
 #define RODIMUS_DEFINE_CHUNK_DK(XK)                                                   \
     size_t chunk_lds_bytes_dk##XK(int dvt, int C, bool f32)                           \
     {                                                                                 \
-        using chunk_detail::Lds;                                                      \
-        if (dvt == 16 && C == 16) return f32 ? Lds<XK, 16, 16, 3>::bytes : Lds<XK, 16, 16, 2>::bytes; \
-        if (dvt == 16 && C == 32) return f32 ? Lds<XK, 16, 32, 3>::bytes : Lds<XK, 16, 32, 2>::bytes; \
-        if (dvt == 16 && C == 64) return f32 ? Lds<XK, 16, 64, 3>::bytes : Lds<XK, 16, 64, 2>::bytes; \
-        if (dvt == 32 && C == 16) return f32 ? Lds<XK, 32, 16, 3>::bytes : Lds<XK, 32, 16, 2>::bytes; \
-        if (dvt == 32 && C == 32) return f32 ? Lds<XK, 32, 32, 3>::bytes : Lds<XK, 32, 32, 2>::bytes; \
-        if (dvt == 32 && C == 64) return f32 ? Lds<XK, 32, 64, 3>::bytes : Lds<XK, 32, 64, 2>::bytes; \
-        if (dvt == 64 && C == 16) return f32 ? Lds<XK, 64, 16, 3>::bytes : Lds<XK, 64, 16, 2>::bytes; \
-        if (dvt == 64 && C == 32) return f32 ? Lds<XK, 64, 32, 3>::bytes : Lds<XK, 64, 32, 2>::bytes; \
-        if (dvt == 64 && C == 64) return f32 ? Lds<XK, 64, 64, 3>::bytes : Lds<XK, 64, 64, 2>::bytes; \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LDS, XK)                              \
         return 0;                                                                     \
     }                                                                                 \
     hipError_t launch_chunk_dk##XK(const ChunkLaunch &Lc, hipStream_t stream)         \
     {                                                                                 \
-        using chunk_detail::launch_t;                                                 \
-        if (Lc.DVT == 16 && Lc.C == 16) return Lc.f32_inputs ? launch_t<XK, 16, 16, float>(Lc, stream) : launch_t<XK, 16, 16, __bf16>(Lc, stream); \
-        if (Lc.DVT == 16 && Lc.C == 32) return Lc.f32_inputs ? launch_t<XK, 16, 32, float>(Lc, stream) : launch_t<XK, 16, 32, __bf16>(Lc, stream); \
-        if (Lc.DVT == 16 && Lc.C == 64) return Lc.f32_inputs ? launch_t<XK, 16, 64, float>(Lc, stream) : launch_t<XK, 16, 64, __bf16>(Lc, stream); \
-        if (Lc.DVT == 32 && Lc.C == 16) return Lc.f32_inputs ? launch_t<XK, 32, 16, float>(Lc, stream) : launch_t<XK, 32, 16, __bf16>(Lc, stream); \
-        if (Lc.DVT == 32 && Lc.C == 32) return Lc.f32_inputs ? launch_t<XK, 32, 32, float>(Lc, stream) : launch_t<XK, 32, 32, __bf16>(Lc, stream); \
-        if (Lc.DVT == 32 && Lc.C == 64) return Lc.f32_inputs ? launch_t<XK, 32, 64, float>(Lc, stream) : launch_t<XK, 32, 64, __bf16>(Lc, stream); \
-        if (Lc.DVT == 64 && Lc.C == 16) return Lc.f32_inputs ? launch_t<XK, 64, 16, float>(Lc, stream) : launch_t<XK, 64, 16, __bf16>(Lc, stream); \
-        if (Lc.DVT == 64 && Lc.C == 32) return Lc.f32_inputs ? launch_t<XK, 64, 32, float>(Lc, stream) : launch_t<XK, 64, 32, __bf16>(Lc, stream); \
-        if (Lc.DVT == 64 && Lc.C == 64) return Lc.f32_inputs ? launch_t<XK, 64, 64, float>(Lc, stream) : launch_t<XK, 64, 64, __bf16>(Lc, stream); \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LAUNCH, XK)                           \
         return hipErrorInvalidValue;                                                  \
     }
 
