@@ -163,6 +163,27 @@ __device__ __forceinline__ f32x4 mma_split(const bf16x8 *A, const bf16x8 *Bv, f3
     return acc;
 }
 
+// Same as mma_split for NT independent tiles, issued term-major so that
+// consecutive MFMAs never depend on each other.
+template <int NS, int NT>
+__device__ __forceinline__ void mma_split_n(const bf16x8 (*A)[NS], const bf16x8 (*Bv)[NS],
+                                            f32x4 *acc) {
+    if constexpr (NS == 3) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][1], Bv[t][1], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[t][2], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][2], Bv[t][0], acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[t][1], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][1], Bv[t][0], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[t][0], acc[t], 0, 0, 0);
+}
+
 struct Args {
     int B, T, H, dv;
     int n_seg, chunks_per_seg, n_chunks, n_jt;
@@ -206,9 +227,6 @@ struct Cfg {
     static constexpr int NG0 = 64 * NP / PP;                  // token groups per column pair
     static constexpr int NG = NG0 < C ? NG0 : C;              // groups actually used
     static constexpr int TPG = C / NG;                        // tokens per group
-    // raw-input register sets of the producers (chunks in flight); a second
-    // set costs more in register spills than it gains in latency hiding
-    static constexpr int PF = 1;
     static constexpr int KSI = (DK + 31) / 32;                // k-steps over dk
     static constexpr int KSC = (C + 31) / 32;                 // k-steps over tokens
     static constexpr int RS = DK + 4;                         // row stride (bf16)
@@ -237,7 +255,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     typedef Pair<TIn> PR;
     typedef typename PR::type Raw2;
     constexpr int NU = L::NU, NI = L::NI, NJ = L::NJ, NA = L::NA, NP = L::NP, PP = L::PP;
-    constexpr int NG = L::NG, TPG = L::TPG, KSI = L::KSI, KSC = L::KSC, PF = L::PF;
+    constexpr int NG = L::NG, TPG = L::TPG, KSI = L::KSI, KSC = L::KSC;
     constexpr int RS = L::RS, MID = L::MID;
     constexpr int esz = sizeof(Raw);
 
@@ -302,31 +320,120 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             for (int r = 0; r < 4; ++r)
                 S[I][r] = (sin && !producer) ? sin[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] : 0.f;
     }
-    float gam_acc0 = 1.f, gam_acc1 = 1.f;               // products of chunk decays (mode 1)
-
-    // ---- raw inputs in registers: producers hold PF chunks of q, k, g, tau
-    // (a dk column pair, TPG consecutive tokens); consumers hold one chunk of
-    // their v, beta_hat columns in MFMA B-operand order (k = tokens).
-    Raw2 rq[PF][TPG], rk[PF][TPG], rg[PF][TPG], rt[PF][TPG];
-    Raw rv[KSC][8], rb[KSC][8];
-    auto load_dk = [&](int ch, auto rsel) {
-        constexpr int R = decltype(rsel)::value;
-        const long long t0 = (long long)ch * C;
-        const long long base = t0 * row_k;
-        const long long lim = ((T - t0) * H - h) * DK * esz;
-        const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
-        const __amdgpu_buffer_rsrc_t Rg = make_rsrc(gg + base, lim);
-        const __amdgpu_buffer_rsrc_t Rt = make_rsrc(gt + base, lim);
-        const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, outputs ? lim : 0);
+    // Pipeline: in iteration it the producers prepare chunk it (LDS buffer
+    // it & 1) while the consumers compute chunk it - 1 (LDS buffer
+    // (it - 1) & 1).  The two roles run separate loops with the same barrier
+    // sequence (two per iteration), so each is register-allocated on its own.
+    if (producer) {
+        // raw inputs of two chunks (the current one and the next, in flight):
+        // a dk column pair, TPG consecutive tokens
+        Raw2 rq[2][TPG], rk[2][TPG], rg[2][TPG], rt[2][TPG];
+        auto load_dk = [&](int ch, auto rsel) {
+            constexpr int R = decltype(rsel)::value;
+            const long long t0 = (long long)ch * C;
+            const long long base = t0 * row_k;
+            const long long lim = ((T - t0) * H - h) * DK * esz;
+            const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
+            const __amdgpu_buffer_rsrc_t Rg = make_rsrc(gg + base, lim);
+            const __amdgpu_buffer_rsrc_t Rt = make_rsrc(gt + base, lim);
+            const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, outputs ? lim : 0);
 #pragma unroll
-        for (int m = 0; m < TPG; ++m) {
-            const unsigned o = off_k + m * step_k;
-            rq[R][m] = PR::load(Rq, o);
-            rk[R][m] = PR::load(Rk, o);
-            rg[R][m] = PR::load(Rg, o);
-            rt[R][m] = PR::load(Rt, o);
+            for (int m = 0; m < TPG; ++m) {
+                const unsigned o = off_k + m * step_k;
+                rg[R][m] = PR::load(Rg, o);
+                rt[R][m] = PR::load(Rt, o);
+                rk[R][m] = PR::load(Rk, o);
+                rq[R][m] = PR::load(Rq, o);
+            }
+        };
+        float gam_acc0 = 1.f, gam_acc1 = 1.f;           // products of chunk decays (mode 1)
+        auto iter = [&](int it, auto rsel) {
+            constexpr int R = decltype(rsel)::value;
+            const bool work = prep && it < c_end;
+            const int pb = it & 1;
+            // the next chunk's inputs load during this whole iteration
+            if (prep && it + 1 < c_end) load_dk(it + 1, std::integral_constant<int, 1 - R>());
+            // ---- phase 1: local cumulative decay of both columns, in log2 units
+            float cum0[TPG], cum1[TPG];
+            if (work) {
+                float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < TPG; ++m) {
+                    run0 = __builtin_fmaf(PR::lo(rg[R][m]) * PR::lo(rt[R][m]), -kLog2e, run0);
+                    run1 = __builtin_fmaf(PR::hi(rg[R][m]) * PR::hi(rt[R][m]), -kLog2e, run1);
+                    cum0[m] = run0;
+                    cum1[m] = run1;
+                }
+                *(float2 *)(sTot + cgp * DK + c0) = make_float2(run0, run1);
+                if (MID / TPG == cgp)
+                    *(float2 *)(sMid + c0) = make_float2(cum0[MID % TPG], cum1[MID % TPG]);
+            }
+            __syncthreads();                               // barrier A
+            // ---- phase 2: gates and scaled operands -> LDS buffer pb
+            if (work) {
+                float off0 = 0.f, off1 = 0.f, bm0 = 0.f, bm1 = 0.f, bL0 = 0.f, bL1 = 0.f;
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    const float2 x = *(const float2 *)(sTot + gi * DK + c0);
+                    if (gi < cgp) { off0 += x.x; off1 += x.y; }
+                    if (gi < MID / TPG) { bm0 += x.x; bm1 += x.y; }
+                    bL0 += x.x; bL1 += x.y;
+                }
+                const float2 mid = *(const float2 *)(sMid + c0);
+                bm0 += mid.x; bm1 += mid.y;
+                const float sh0 = off0 - bm0, sh1 = off1 - bm1;
+                __bf16 *qb = bQ(pb), *kb = bK(pb);
+#pragma unroll
+                for (int m = 0; m < TPG; ++m) {
+                    const int u = cgp * TPG + m;
+                    const float d0 = cum0[m] + sh0, d1 = cum1[m] + sh1;          // b_u - b_m
+                    const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
+                    const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
+                    __bf16 p0[NS], p1[NS];
+                    split<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0), p0);
+                    split<NS>(PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), p1);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        __bf16 pr[2] = {p0[n], p1[n]};
+                        *(unsigned *)(kb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
+                    }
+                    if (outputs) {
+                        split<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0), p0);
+                        split<NS>(PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), p1);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            __bf16 pr[2] = {p0[n], p1[n]};
+                            *(unsigned *)(qb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
+                        }
+                    }
+                }
+                if (cgp == 0) {
+                    const float g0 = __builtin_amdgcn_exp2f(bL0), g1 = __builtin_amdgcn_exp2f(bL1);
+                    *(float2 *)(bGam(pb) + c0) = make_float2(g0, g1);
+                    *(float2 *)(bEm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bm0),
+                                                            __builtin_amdgcn_exp2f(bm1));
+                    *(float2 *)(bGm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bL0 - bm0),
+                                                            __builtin_amdgcn_exp2f(bL1 - bm1));
+                    gam_acc0 *= g0;
+                    gam_acc1 *= g1;
+                }
+            }
+            __syncthreads();                               // barrier B
+        };
+        if (prep && c_begin < c_end) load_dk(c_begin, std::integral_constant<int, 0>());
+        for (int it = c_begin; it <= c_end; it += 2) {
+            iter(it, std::integral_constant<int, 0>());
+            if (it + 1 <= c_end) iter(it + 1, std::integral_constant<int, 1>());
         }
-    };
+        if (!outputs && a.gam_out && jt == 0 && prep && cgp == 0)
+            *(float2 *)(a.gam_out + ((size_t)bh * a.n_seg + seg) * DK + c0) =
+                make_float2(gam_acc0, gam_acc1);
+        return;
+    }
+
+    // ================= consumers
+    // this wave's v, beta_hat columns for one chunk, in MFMA B-operand order
+    Raw rv[KSC][8], rb[KSC][8];
     auto load_v = [&](int ch) {
         const long long t0 = (long long)ch * C;
         const long long base = t0 * row_v;
@@ -348,44 +455,15 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                 }
             }
     };
-    typedef std::integral_constant<int, 0> R0;
-    typedef std::integral_constant<int, PF - 1> R1;
+    if (c_begin < c_end) load_v(c_begin);
 
-    if (c_begin < c_end) {
-        if (prep) {
-            load_dk(c_begin, R0());
-            if (PF == 2 && c_begin + 1 < c_end) load_dk(c_begin + 1, R1());
-        }
-        if (!producer) load_v(c_begin);
-    }
-
-    // Pipeline: in iteration it the producers prepare chunk it (LDS buffer
-    // it & 1, raw registers (it - c_begin) % PF) while the consumers compute
-    // chunk it - 1 (LDS buffer (it - 1) & 1).
-    auto body = [&](int it, auto rsel) {
-        constexpr int R = decltype(rsel)::value;
-        const bool pwork = it < c_end;
+    for (int it = c_begin; it <= c_end; ++it) {
         const bool cwork = it > c_begin;
-        const int pb = it & 1, cb = (it - 1) & 1;
+        const int cb = (it - 1) & 1;
 
-        // ================= phase 1
-        float cum0[TPG], cum1[TPG];
+        // ================= phase 1: S' operands and the A^T tiles of this wave
         bf16x8 sB[KSI][NS];
-        if (prep && pwork) {
-            // local cumulative decay of both columns, in log2 units
-            float run0 = 0.f, run1 = 0.f;
-#pragma unroll
-            for (int m = 0; m < TPG; ++m) {
-                run0 = __builtin_fmaf(PR::lo(rg[R][m]) * PR::lo(rt[R][m]), -kLog2e, run0);
-                run1 = __builtin_fmaf(PR::hi(rg[R][m]) * PR::hi(rt[R][m]), -kLog2e, run1);
-                cum0[m] = run0;
-                cum1[m] = run1;
-            }
-            *(float2 *)(sTot + cgp * DK + c0) = make_float2(run0, run1);
-            if (MID / TPG == cgp)
-                *(float2 *)(sMid + c0) = make_float2(cum0[MID % TPG], cum1[MID % TPG]);
-        }
-        if (!producer && cwork && outputs) {
+        if (cwork && outputs) {
             // B operands S' = diag(exp(b_m)) S_in (k = dk rows)
             const float *em = bEm(cb);
 #pragma unroll
@@ -454,58 +532,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
         __syncthreads();                                   // barrier A
 
         // ================= phase 2
-        if (producer) {
-            if (prep && pwork) {
-                float off0 = 0.f, off1 = 0.f, bm0 = 0.f, bm1 = 0.f, bL0 = 0.f, bL1 = 0.f;
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    const float2 x = *(const float2 *)(sTot + gi * DK + c0);
-                    if (gi < cgp) { off0 += x.x; off1 += x.y; }
-                    if (gi < MID / TPG) { bm0 += x.x; bm1 += x.y; }
-                    bL0 += x.x; bL1 += x.y;
-                }
-                const float2 mid = *(const float2 *)(sMid + c0);
-                bm0 += mid.x; bm1 += mid.y;
-                const float sh0 = off0 - bm0, sh1 = off1 - bm1;
-                __bf16 *qb = bQ(pb), *kb = bK(pb);
-#pragma unroll
-                for (int m = 0; m < TPG; ++m) {
-                    const int u = cgp * TPG + m;
-                    const float d0 = cum0[m] + sh0, d1 = cum1[m] + sh1;          // b_u - b_m
-                    // log2 of alpha_hat = tau * log2(g) (0 when tau = 0, also at g = 0)
-                    const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
-                    const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
-                    __bf16 p0[NS], p1[NS];
-                    split<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0), p0);
-                    split<NS>(PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), p1);
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        __bf16 pr[2] = {p0[n], p1[n]};
-                        *(unsigned *)(kb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
-                    }
-                    if (outputs) {
-                        split<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0), p0);
-                        split<NS>(PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), p1);
-#pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            __bf16 pr[2] = {p0[n], p1[n]};
-                            *(unsigned *)(qb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
-                        }
-                    }
-                }
-                if (cgp == 0) {
-                    const float g0 = __builtin_amdgcn_exp2f(bL0), g1 = __builtin_amdgcn_exp2f(bL1);
-                    *(float2 *)(bGam(pb) + c0) = make_float2(g0, g1);
-                    *(float2 *)(bEm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bm0),
-                                                            __builtin_amdgcn_exp2f(bm1));
-                    *(float2 *)(bGm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bL0 - bm0),
-                                                            __builtin_amdgcn_exp2f(bL1 - bm1));
-                    gam_acc0 *= g0;
-                    gam_acc1 *= g1;
-                }
-            }
-            if (prep && it + PF < c_end) load_dk(it + PF, rsel);
-        } else if (cwork) {
+        if (cwork) {
             const long long t0 = (long long)(it - 1) * C;
             // V' = beta_hat * v of this wave's columns, as split B operands (k = tokens)
             bf16x8 vB[KSC][NS];
@@ -527,90 +554,110 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             if (it < c_end) load_v(it);                     // next chunk's v, beta_hat
 
             // dS = diag(exp(b_L - b_m)) Kt^T V' and S = diag(exp(b_L)) S + dS;
-            // Kt^T is read with the transposing LDS read (k = tokens)
-            const __bf16 *kb = bK(cb);
-            const float *gam = bGam(cb), *gmv = bGm(cb);
-            const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
+            // Kt^T is read with the transposing LDS read (k = tokens).  The NI
+            // row tiles are independent accumulators, issued interleaved.
+            {
+                const __bf16 *kb = bK(cb);
+                const float *gam = bGam(cb), *gmv = bGm(cb);
+                const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
+                f32x4 acc[NI];
 #pragma unroll
-            for (int I = 0; I < NI; ++I) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int I = 0; I < NI; ++I) acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks) {
                     const int s_lo = ks * 32 + trow, s_hi = s_lo + 16;
-                    bf16x8 A[NS];
+                    bf16x8 A[NI][NS], Bv[NI][NS];
 #pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        const __bf16 *base = kb + n * C * RS + I * 16 + tcol;
-                        const bf16x4 klo = lds_read_tr(base + s_lo * RS);
-                        const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
-                        A[n] = cat(klo, khi);
-                    }
-                    acc = mma_split<NS>(A, vB[ks], acc);
+                    for (int I = 0; I < NI; ++I)
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const __bf16 *base = kb + n * C * RS + I * 16 + tcol;
+                            const bf16x4 klo = lds_read_tr(base + s_lo * RS);
+                            const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
+                            A[I][n] = cat(klo, khi);
+                            Bv[I][n] = vB[ks][n];
+                        }
+                    mma_split_n<NS, NI>(A, Bv, acc);
                 }
-                const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
-                const f32x4 g1 = *(const f32x4 *)(gmv + I * 16 + 4 * lg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[r], g0[r] * S[I][r]);
+                for (int I = 0; I < NI; ++I) {
+                    const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
+                    const f32x4 g1 = *(const f32x4 *)(gmv + I * 16 + 4 * lg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[I][r], g0[r] * S[I][r]);
+                }
             }
 
             if (outputs) {
-                // O = A V' + Qt S' for this wave's columns
+                // O = A V' + Qt S' for this wave's columns; the NU token tiles
+                // are independent accumulators, issued interleaved.
                 const long long lim = ((T - t0) * H - h) * dv * 4 - (long long)jcol * 4;
                 const __amdgpu_buffer_rsrc_t Ro = make_rsrc(go + t0 * row_v, lim);
                 const __bf16 *qb = bQ(cb);
+                f32x4 acc[NU];
 #pragma unroll
-                for (int Ub = 0; Ub < NU; ++Ub) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    // intra-chunk: k = s over token blocks 0..Ub, two 16-blocks per step
+                for (int U = 0; U < NU; ++U) acc[U] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // inter-chunk: k = i, A = Qt rows, B = S'
 #pragma unroll
-                    for (int p = 0; p <= Ub / 2; ++p) {
-                        const int S1 = 2 * p + 1;
-                        const int t0x = Ub * (Ub + 1) / 2 + 2 * p;
-                        bf16x8 A[NS], Bv[NS];
+                for (int ks = 0; ks < KSI; ++ks) {
+                    const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
+                    bf16x8 A[NU][NS], Bv[NU][NS];
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const bf16x4 alo = *(const bf16x4 *)(sA + ((t0x * NS + n) * 64 + lane) * 4);
-                            const bf16x4 ahi = S1 <= Ub
-                                ? *(const bf16x4 *)(sA + (((t0x + 1) * NS + n) * 64 + lane) * 4) : zero4();
-                            A[n] = cat(alo, ahi);
-                            Bv[n] = vB[p][n];
-                            if (S1 > Ub)           // keep only the first 16 tokens of this k-step
-                                for (int e = 4; e < 8; ++e) Bv[n][e] = (__bf16)0.f;
-                        }
-                        acc = mma_split<NS>(A, Bv, acc);
-                    }
-                    // inter-chunk: k = i, A = Qt rows, B = S'
-#pragma unroll
-                    for (int ks = 0; ks < KSI; ++ks) {
-                        const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
-                        bf16x8 A[NS];
+                    for (int U = 0; U < NU; ++U)
 #pragma unroll
                         for (int n = 0; n < NS; ++n) {
-                            const __bf16 *qr = qb + (n * C + Ub * 16 + lc) * RS;
+                            const __bf16 *qr = qb + (n * C + U * 16 + lc) * RS;
                             const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
                             const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
-                            A[n] = cat(qlo, qhi);
+                            A[U][n] = cat(qlo, qhi);
+                            Bv[U][n] = sB[ks][n];
                         }
-                        acc = mma_split<NS>(A, sB[ks], acc);
-                    }
+                    mma_split_n<NS, NU>(A, Bv, acc);
+                }
+                // intra-chunk: k = s over token blocks 2p, 2p+1 for the tiles U >= 2p
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const unsigned o = (unsigned)((((long long)(Ub * 16 + 4 * lg + r)) * row_v + lc) * 4);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), Ro, o, 0, 0);
+                for (int p = 0; p < KSC; ++p) {
+                    constexpr int NUP = NU;             // tiles with U >= 2p, padded to NU
+                    bf16x8 A[NUP][NS], Bv[NUP][NS];
+#pragma unroll
+                    for (int U = 0; U < NU; ++U) {
+                        const bool live = 2 * p <= U;
+                        const int t0x = U * (U + 1) / 2 + 2 * p;
+                        const bool two = 2 * p + 1 <= U;
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            if (live) {
+                                const bf16x4 alo = *(const bf16x4 *)(sA + ((t0x * NS + n) * 64 + lane) * 4);
+                                const bf16x4 ahi = two
+                                    ? *(const bf16x4 *)(sA + (((t0x + 1) * NS + n) * 64 + lane) * 4) : zero4();
+                                A[U][n] = cat(alo, ahi);
+                                Bv[U][n] = vB[p][n];
+                                if (!two)          // keep only the first 16 tokens of this k-step
+                                    for (int e = 4; e < 8; ++e) Bv[U][n][e] = (__bf16)0.f;
+                            }
+                        }
+                    }
+                    // tiles U < 2p take no part in this k-step
+                    if (p == 0) {
+                        mma_split_n<NS, NU>(A, Bv, acc);
+                    } else {
+                        mma_split_n<NS, NU - 2>(A + 2, Bv + 2, acc + 2);
                     }
                 }
+#pragma unroll
+                for (int U = 0; U < NU; ++U)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const unsigned o = (unsigned)((((long long)(U * 16 + 4 * lg + r)) * row_v + lc) * 4);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[U][r]), Ro, o, 0, 0);
+                    }
             }
         }
         __syncthreads();                                   // barrier B
-    };
-
-    for (int it = c_begin; it <= c_end; it += PF) {
-        body(it, R0());
-        if (PF == 2 && it + 1 <= c_end) body(it + 1, R1());
     }
 
     // ---- state out
-    if (!producer && a.s_out && (!a.s_out_last_only || seg == a.n_seg - 1)) {
+    if (a.s_out && (!a.s_out_last_only || seg == a.n_seg - 1)) {
         float *so = a.s_out + bh * a.s_out_bh + seg * a.s_out_seg;
 #pragma unroll
         for (int I = 0; I < NI; ++I)
@@ -618,8 +665,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             for (int r = 0; r < 4; ++r)
                 so[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] = S[I][r];
     }
-    if (!outputs && a.gam_out && jt == 0 && prep && cgp == 0)
-        *(float2 *)(a.gam_out + ((size_t)bh * a.n_seg + seg) * DK + c0) = make_float2(gam_acc0, gam_acc1);
 }
 
 template <int DK, int DVT, int C, typename TIn>
