@@ -123,17 +123,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, long 
     return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, n, kBufFlags);
 }
 
-// Split x into NS bf16 terms, x ~= p[0] + p[1] (+ p[2]); each residual is exact in fp32.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Split two fp32 values into NS packed bf16 pairs: out[n] holds term n of x0
+// (low half) and of x1 (high half); x ~= sum of the terms, residuals exact in
+// fp32 (round-to-nearest-even conversion, v_cvt_pk_bf16_f32).
 template <int NS>
-__device__ __forceinline__ void split(float x, __bf16 *p) {
-    const __bf16 h = (__bf16)x;
-    p[0] = h;
-    if constexpr (NS > 1) {
-        const float r = x - (float)h;
-        const __bf16 m = (__bf16)r;
-        p[1] = m;
-        if constexpr (NS > 2) p[2] = (__bf16)(r - (float)m);
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned *out) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 x = {x0, x1};
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        const unsigned hu = __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf2));
+        out[n] = hu;
+        if (n + 1 < NS) {
+            x[0] -= __uint_as_float(hu << 16);
+            x[1] -= __uint_as_float(hu & 0xffff0000u);
+        }
     }
+}
+
+__device__ __forceinline__ bf16x8 pack8(unsigned a, unsigned b, unsigned c, unsigned d) {
+    return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
@@ -389,22 +401,16 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                     const float d0 = cum0[m] + sh0, d1 = cum1[m] + sh1;          // b_u - b_m
                     const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
                     const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
-                    __bf16 p0[NS], p1[NS];
-                    split<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0), p0);
-                    split<NS>(PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), p1);
+                    unsigned pk[NS];
+                    split_pair<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0),
+                                   PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), pk);
 #pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        __bf16 pr[2] = {p0[n], p1[n]};
-                        *(unsigned *)(kb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
-                    }
+                    for (int n = 0; n < NS; ++n) *(unsigned *)(kb + (n * C + u) * RS + c0) = pk[n];
                     if (outputs) {
-                        split<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0), p0);
-                        split<NS>(PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), p1);
+                        split_pair<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0),
+                                       PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), pk);
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            __bf16 pr[2] = {p0[n], p1[n]};
-                            *(unsigned *)(qb + (n * C + u) * RS + c0) = __builtin_bit_cast(unsigned, pr);
-                        }
+                        for (int n = 0; n < NS; ++n) *(unsigned *)(qb + (n * C + u) * RS + c0) = pk[n];
                     }
                 }
                 if (cgp == 0) {
@@ -468,64 +474,77 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             const float *em = bEm(cb);
 #pragma unroll
             for (int ks = 0; ks < KSI; ++ks) {
-                const int I0 = 2 * ks, I1 = 2 * ks + 1;
+                const int I0 = 2 * ks, I1 = 2 * ks + 1 < NI ? 2 * ks + 1 : 2 * ks;
                 const f32x4 e0 = *(const f32x4 *)(em + I0 * 16 + 4 * lg);
-                f32x4 e1 = {0.f, 0.f, 0.f, 0.f};
-                if (I1 < NI) e1 = *(const f32x4 *)(em + I1 * 16 + 4 * lg);
+                const f32x4 e1 = 2 * ks + 1 < NI ? *(const f32x4 *)(em + I1 * 16 + 4 * lg)
+                                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+                unsigned w0[NS], w1[NS], w2[NS], w3[NS];
+                split_pair<NS>(S[I0][0] * e0[0], S[I0][1] * e0[1], w0);
+                split_pair<NS>(S[I0][2] * e0[2], S[I0][3] * e0[3], w1);
+                split_pair<NS>(S[I1][0] * e1[0], S[I1][1] * e1[1], w2);
+                split_pair<NS>(S[I1][2] * e1[2], S[I1][3] * e1[3], w3);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    __bf16 t0_[NS], t1_[NS];
-                    split<NS>(S[I0][r] * e0[r], t0_);
-                    split<NS>(I1 < NI ? S[I1 < NI ? I1 : 0][r] * e1[r] : 0.f, t1_);
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        sB[ks][n][r] = t0_[n];
-                        sB[ks][n][4 + r] = t1_[n];
-                    }
-                }
+                for (int n = 0; n < NS; ++n) sB[ks][n] = pack8(w0[n], w1[n], w2[n], w3[n]);
             }
-            // A^T tiles (Sb, Ub), Sb <= Ub: rows s of Kt, columns u of Qt, k = i
+            // A^T tiles (Sb, Ub), Sb <= Ub (rows s of Kt, columns u of Qt, k = i):
+            // this wave takes tiles cw, cw + NJ, ..., in interleaved groups
+            constexpr int TPW = (NA + NJ - 1) / NJ;            // tiles per wave
+            constexpr int G = TPW < 4 ? TPW : 4;               // interleave group
             const __bf16 *qb = bQ(cb), *kb = bK(cb);
 #pragma unroll
-            for (int Ub = 0; Ub < NU; ++Ub) {
+            for (int j0 = 0; j0 < TPW; j0 += G) {
+                int sbv[G], ubv[G];
+                bool live[G];
 #pragma unroll
-                for (int Sb = 0; Sb <= Ub; ++Sb) {
-                    const int tix = Ub * (Ub + 1) / 2 + Sb;
-                    if (tix % NJ != cw) continue;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < G; ++j) {
+                    int tix = cw + NJ * (j0 + j);
+                    live[j] = j0 + j < TPW && tix < NA;
+                    if (!live[j]) tix = 0;
+                    // tile index -> (Sb, Ub): tix = Ub (Ub + 1) / 2 + Sb
+                    int ub = 0;
 #pragma unroll
-                    for (int ks = 0; ks < KSI; ++ks) {
-                        const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
-                        bf16x8 A[NS], Bv[NS];
+                    for (int q = 1; q < NU; ++q) ub += tix >= q * (q + 1) / 2 ? 1 : 0;
+                    ubv[j] = ub;
+                    sbv[j] = tix - ub * (ub + 1) / 2;
+                }
+                f32x4 acc[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 A[KSI][G][NS], Bq[KSI][G][NS];
+#pragma unroll
+                for (int ks = 0; ks < KSI; ++ks) {
+                    const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
+#pragma unroll
+                    for (int j = 0; j < G; ++j)
 #pragma unroll
                         for (int n = 0; n < NS; ++n) {
-                            const __bf16 *kr = kb + (n * C + Sb * 16 + lc) * RS;
-                            const __bf16 *qr = qb + (n * C + Ub * 16 + lc) * RS;
+                            const __bf16 *kr = kb + (n * C + sbv[j] * 16 + lc) * RS;
+                            const __bf16 *qr = qb + (n * C + ubv[j] * 16 + lc) * RS;
                             const bf16x4 klo = *(const bf16x4 *)(kr + i_lo);
                             const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
                             const bf16x4 khi = i_hi < DK ? *(const bf16x4 *)(kr + i_hi) : zero4();
                             const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
-                            A[n] = cat(klo, khi);
-                            Bv[n] = cat(qlo, qhi);
+                            A[ks][j][n] = cat(klo, khi);
+                            Bq[ks][j][n] = cat(qlo, qhi);
                         }
-                        acc = mma_split<NS>(A, Bv, acc);
-                    }
-                    __bf16 pl[NS][4];
+                }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = acc[r];
-                        if (Sb == Ub && 4 * lg + r > lc) x = 0.f;     // causal: keep s <= u
-                        __bf16 p[NS];
-                        split<NS>(x, p);
+                for (int ks = 0; ks < KSI; ++ks) mma_split_n<NS, G>(A[ks], Bq[ks], acc);
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) pl[n][r] = p[n];
-                    }
+                for (int j = 0; j < G; ++j) {
+                    if (!live[j]) continue;
+                    const int tix = ubv[j] * (ubv[j] + 1) / 2 + sbv[j];
+                    const bool diag = sbv[j] == ubv[j];
+                    float x[4];
 #pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        bf16x4 w;
-                        w[0] = pl[n][0]; w[1] = pl[n][1]; w[2] = pl[n][2]; w[3] = pl[n][3];
-                        *(bf16x4 *)(sA + ((tix * NS + n) * 64 + lane) * 4) = w;
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        x[r] = (diag && 4 * lg + r > lc) ? 0.f : acc[j][r];   // causal: s <= u
+                    unsigned w0[NS], w1[NS];
+                    split_pair<NS>(x[0], x[1], w0);
+                    split_pair<NS>(x[2], x[3], w1);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n)
+                        *(uint2 *)(sA + ((tix * NS + n) * 64 + lane) * 4) = make_uint2(w0[n], w1[n]);
                 }
             }
         }
@@ -538,18 +557,13 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             bf16x8 vB[KSC][NS];
 #pragma unroll
             for (int p = 0; p < KSC; ++p) {
-                __bf16 pl[NS][8];
+                unsigned w[4][NS];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 t[NS];
-                    split<NS>(in_to_f32(rb[p][e]) * in_to_f32(rv[p][e]), t);
+                for (int e = 0; e < 4; ++e)
+                    split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e]),
+                                   in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1]), w[e]);
 #pragma unroll
-                    for (int n = 0; n < NS; ++n) pl[n][e] = t[n];
-                }
-#pragma unroll
-                for (int n = 0; n < NS; ++n)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vB[p][n][e] = pl[n][e];
+                for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
             }
             if (it < c_end) load_v(it);                     // next chunk's v, beta_hat
 
@@ -563,10 +577,10 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                 f32x4 acc[NI];
 #pragma unroll
                 for (int I = 0; I < NI; ++I) acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                bf16x8 A[KSC][NI][NS], Bv[KSC][NI][NS];
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks) {
                     const int s_lo = ks * 32 + trow, s_hi = s_lo + 16;
-                    bf16x8 A[NI][NS], Bv[NI][NS];
 #pragma unroll
                     for (int I = 0; I < NI; ++I)
 #pragma unroll
@@ -574,11 +588,12 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                             const __bf16 *base = kb + n * C * RS + I * 16 + tcol;
                             const bf16x4 klo = lds_read_tr(base + s_lo * RS);
                             const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
-                            A[I][n] = cat(klo, khi);
-                            Bv[I][n] = vB[ks][n];
+                            A[ks][I][n] = cat(klo, khi);
+                            Bv[ks][I][n] = vB[ks][n];
                         }
-                    mma_split_n<NS, NI>(A, Bv, acc);
                 }
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) mma_split_n<NS, NI>(A[ks], Bv[ks], acc);
 #pragma unroll
                 for (int I = 0; I < NI; ++I) {
                     const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
@@ -598,21 +613,24 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 #pragma unroll
                 for (int U = 0; U < NU; ++U) acc[U] = f32x4{0.f, 0.f, 0.f, 0.f};
                 // inter-chunk: k = i, A = Qt rows, B = S'
+                {
+                    bf16x8 A[KSI][NU][NS], Bv[KSI][NU][NS];
 #pragma unroll
-                for (int ks = 0; ks < KSI; ++ks) {
-                    const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
-                    bf16x8 A[NU][NS], Bv[NU][NS];
+                    for (int ks = 0; ks < KSI; ++ks) {
+                        const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
 #pragma unroll
-                    for (int U = 0; U < NU; ++U)
+                        for (int U = 0; U < NU; ++U)
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const __bf16 *qr = qb + (n * C + U * 16 + lc) * RS;
-                            const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
-                            const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
-                            A[U][n] = cat(qlo, qhi);
-                            Bv[U][n] = sB[ks][n];
-                        }
-                    mma_split_n<NS, NU>(A, Bv, acc);
+                            for (int n = 0; n < NS; ++n) {
+                                const __bf16 *qr = qb + (n * C + U * 16 + lc) * RS;
+                                const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
+                                const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
+                                A[ks][U][n] = cat(qlo, qhi);
+                                Bv[ks][U][n] = sB[ks][n];
+                            }
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KSI; ++ks) mma_split_n<NS, NU>(A[ks], Bv[ks], acc);
                 }
                 // intra-chunk: k = s over token blocks 2p, 2p+1 for the tiles U >= 2p
 #pragma unroll
