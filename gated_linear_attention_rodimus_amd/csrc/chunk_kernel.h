@@ -253,7 +253,10 @@ struct Cfg {
     static constexpr size_t a_off = 2 * buf_bytes;
     static constexpr size_t tot_off = a_off + (size_t)NA * NS * 64 * 4 * 2;
     static constexpr size_t mid_off = tot_off + (size_t)NG * DK * 4;
-    static constexpr size_t bytes = mid_off + (size_t)DK * 4;
+    // per consumer wave: raw v and beta_hat of one chunk, [C][16] bf16 each
+    static constexpr size_t stg_off = mid_off + (size_t)DK * 4;
+    static constexpr size_t stg_wave = (size_t)2 * C * 16 * 2;
+    static constexpr size_t bytes = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
@@ -439,27 +442,50 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 
     // ================= consumers
     // this wave's v, beta_hat columns for one chunk, in MFMA B-operand order
+    // bf16 inputs: 16-byte loads of whole [token][16 columns] rows (lane l:
+    // token l/2 + 32 j, columns 8 (l & 1)..+7), staged per wave in LDS and read
+    // back in B-operand order with the transposing read.  fp32 inputs: one
+    // element per load, straight into B-operand order.
+    constexpr bool kStage = NS == 2;
+    constexpr int LV = C >= 32 ? C / 32 : 1;             // 16-byte loads per tensor
+    u32x4 rvw[LV], rbw[LV];
     Raw rv[KSC][8], rb[KSC][8];
+    __bf16 *stg = (__bf16 *)(smem + L::stg_off + (size_t)(producer ? 0 : cw) * L::stg_wave);
     auto load_v = [&](int ch) {
         const long long t0 = (long long)ch * C;
         const long long base = t0 * row_v;
         const long long lim = ((T - t0) * H - h) * dv * esz - (long long)jcol * esz;
         const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lim);
         const __amdgpu_buffer_rsrc_t Rb = make_rsrc(gb + base, lim);
+        if constexpr (kStage) {
 #pragma unroll
-        for (int p = 0; p < KSC; ++p)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int u = p * 32 + (e < 4 ? e : 12 + e);            // + 4*lg via off_v
+            for (int j = 0; j < LV; ++j) {
+                const int u = (lane >> 1) + 32 * j;
+                const unsigned o = (unsigned)(((long long)u * row_v + 8 * (lane & 1)) * esz);
                 if (u < C) {
-                    const unsigned o = off_v + u * step_v;
-                    rv[p][e] = buf_load(Rv, o, Raw());
-                    rb[p][e] = buf_load(Rb, o, Raw());
+                    rvw[j] = __builtin_amdgcn_raw_buffer_load_b128(Rv, o, 0, 0);
+                    rbw[j] = __builtin_amdgcn_raw_buffer_load_b128(Rb, o, 0, 0);
                 } else {
-                    rv[p][e] = Raw(0);
-                    rb[p][e] = Raw(0);
+                    rvw[j] = u32x4{0u, 0u, 0u, 0u};
+                    rbw[j] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
+        } else {
+#pragma unroll
+            for (int p = 0; p < KSC; ++p)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int u = p * 32 + (e < 4 ? e : 12 + e);            // + 4*lg via off_v
+                    if (u < C) {
+                        const unsigned o = off_v + u * step_v;
+                        rv[p][e] = buf_load(Rv, o, Raw());
+                        rb[p][e] = buf_load(Rb, o, Raw());
+                    } else {
+                        rv[p][e] = Raw(0);
+                        rb[p][e] = Raw(0);
+                    }
+                }
+        }
     };
     if (c_begin < c_end) load_v(c_begin);
 
@@ -555,15 +581,44 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             const long long t0 = (long long)(it - 1) * C;
             // V' = beta_hat * v of this wave's columns, as split B operands (k = tokens)
             bf16x8 vB[KSC][NS];
+            if constexpr (kStage) {
+                // stage this wave's rows, then read them back token-major
 #pragma unroll
-            for (int p = 0; p < KSC; ++p) {
-                unsigned w[4][NS];
+                for (int j = 0; j < LV; ++j) {
+                    const int u = (lane >> 1) + 32 * j;
+                    if (u < C) {
+                        *(u32x4 *)(stg + u * 16 + 8 * (lane & 1)) = rvw[j];
+                        *(u32x4 *)(stg + C * 16 + u * 16 + 8 * (lane & 1)) = rbw[j];
+                    }
+                }
+                const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e]),
-                                   in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1]), w[e]);
+                for (int p = 0; p < KSC; ++p) {
+                    const int r0 = 32 * p + trow;
+                    const bool hi = 32 * p + 16 < C;
+                    const bf16x4 v0 = lds_read_tr(stg + r0 * 16 + tcol);
+                    const bf16x4 b0 = lds_read_tr(stg + C * 16 + r0 * 16 + tcol);
+                    const bf16x4 v1 = hi ? lds_read_tr(stg + (r0 + 16) * 16 + tcol) : zero4();
+                    const bf16x4 b1 = hi ? lds_read_tr(stg + C * 16 + (r0 + 16) * 16 + tcol) : zero4();
+                    unsigned w[4][NS];
+                    split_pair<NS>((float)v0[0] * (float)b0[0], (float)v0[1] * (float)b0[1], w[0]);
+                    split_pair<NS>((float)v0[2] * (float)b0[2], (float)v0[3] * (float)b0[3], w[1]);
+                    split_pair<NS>((float)v1[0] * (float)b1[0], (float)v1[1] * (float)b1[1], w[2]);
+                    split_pair<NS>((float)v1[2] * (float)b1[2], (float)v1[3] * (float)b1[3], w[3]);
 #pragma unroll
-                for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
+                    for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < KSC; ++p) {
+                    unsigned w[4][NS];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e]),
+                                       in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1]), w[e]);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
+                }
             }
             if (it < c_end) load_v(it);                     // next chunk's v, beta_hat
 
