@@ -67,6 +67,8 @@ namespace rodimus {
 namespace chunk_detail {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt unlimited
+constexpr int kWaitVmcnt0 = 0x0f70;
 constexpr int kBufFlags = 0x00020000;          // raw buffer, 32-bit data format (gfx9)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -88,6 +90,14 @@ __device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, unsigned off
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Dot product of two packed bf16 pairs accumulated into an fp32 value,
+// a.lo * b.lo + a.hi * b.hi + c (v_dot2c_f32_bf16); the products are exact.
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b), c,
+                                          false);
+}
+
 // Two adjacent elements of a per-token input: one 32-bit word for bf16, two
 // for fp32.
 template <typename TIn> struct Pair;
@@ -98,6 +108,14 @@ template <> struct Pair<__bf16> {
     }
     static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x << 16); }
     static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x & 0xffff0000u); }
+    // run + g * t of the low / high elements (one packed dot product each; the
+    // operands are the unpacked words, i.e. pairs (0, x))
+    static __device__ __forceinline__ float gt_lo(type g, type t, float run) {
+        return dot2_bf16(g << 16, t << 16, run);
+    }
+    static __device__ __forceinline__ float gt_hi(type g, type t, float run) {
+        return dot2_bf16(g & 0xffff0000u, t & 0xffff0000u, run);
+    }
 };
 template <> struct Pair<float> {
     typedef unsigned type __attribute__((ext_vector_type(2)));
@@ -106,6 +124,12 @@ template <> struct Pair<float> {
     }
     static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x[0]); }
     static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x[1]); }
+    static __device__ __forceinline__ float gt_lo(type g, type t, float run) {
+        return __builtin_fmaf(lo(g), lo(t), run);
+    }
+    static __device__ __forceinline__ float gt_hi(type g, type t, float run) {
+        return __builtin_fmaf(hi(g), hi(t), run);
+    }
 };
 
 // Buffer resource over [p, p + bytes); bytes is clamped to 31 bits.  The
@@ -125,9 +149,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, long 
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// A constant materialised in an SGPR by an instruction the optimiser does not
+// look through (so a dot product with it is not rewritten into other forms).
+template <unsigned V>
+__device__ __forceinline__ unsigned sgpr_const() {
+    unsigned r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+    return r;
+}
+
 // Split two fp32 values into NS packed bf16 pairs: out[n] holds term n of x0
-// (low half) and of x1 (high half); x ~= sum of the terms, residuals exact in
-// fp32 (round-to-nearest-even conversion, v_cvt_pk_bf16_f32).
+// (low half) and of x1 (high half); x ~= sum of the terms.  Each term is the
+// round-to-nearest-even bf16 of the remaining residual (v_cvt_pk_bf16_f32); the
+// residual x - term is exact in fp32 and is formed by one packed dot product
+// with the constant pair (-1, 0) or (0, -1).
 template <int NS>
 __device__ __forceinline__ void split_pair(float x0, float x1, unsigned *out) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -138,8 +173,8 @@ __device__ __forceinline__ void split_pair(float x0, float x1, unsigned *out) {
         const unsigned hu = __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf2));
         out[n] = hu;
         if (n + 1 < NS) {
-            x[0] -= __uint_as_float(hu << 16);
-            x[1] -= __uint_as_float(hu & 0xffff0000u);
+            x[0] = dot2_bf16(hu, sgpr_const<0x0000bf80u>(), x[0]);   // x0 - term (low half)
+            x[1] = dot2_bf16(hu, sgpr_const<0xbf800000u>(), x[1]);   // x1 - term (high half)
         }
     }
 }
@@ -261,7 +296,7 @@ struct Cfg {
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
 
-template <int DK, int DVT, int C, typename TIn>
+template <int DK, int DVT, int C, typename TIn, bool OUT>
 __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(Args a)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
@@ -296,7 +331,10 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     const int b = bh / a.H, h = bh % a.H;
     const int c_begin = seg * a.chunks_per_seg;
     const int c_end = min(a.n_chunks, c_begin + a.chunks_per_seg);
-    const bool outputs = a.mode == 0;
+    // pipeline steps: one per chunk plus one to drain, rounded up to even for
+    // the producers' two-step loop (the extra step only meets the barriers)
+    const int n_iter = (c_end - c_begin + 2) & ~1;
+    constexpr bool outputs = OUT;           // mode 0: outputs; mode 1: segment transfer
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -308,6 +346,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     const int cp = tid % PP, cgp = tid / PP;           // producer: dk column pair owner
     const int c0 = 2 * cp;                             // its columns c0, c0 + 1
     const bool prep = producer && cgp < NG;
+    constexpr bool kAllPrep = NG * PP == 64 * NP;          // every producer lane has a group
 
     const long long T = a.T, H = a.H, dv = a.dv;
     const long long row_k = H * DK, row_v = H * dv;    // elements between tokens
@@ -334,31 +373,105 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[I][r] = (sin && !producer) ? sin[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] : 0.f;
+        // complete these loads here: a wait for them placed inside the chunk
+        // loop would also wait for every output store still in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
+    // A^T tiles (Sb, Ub), Sb <= Ub, of the chunk in LDS buffer cb (rows s of Kt,
+    // columns u of Qt, k = i), causally masked and stored split in sA as MFMA
+    // A-operand register images.  Producer wave wi takes tiles wi, wi + NP, ...,
+    // in interleaved groups.
+    auto score_tiles = [&](int wi, int cb) {
+        constexpr int TPW = (NA + NP - 1) / NP;            // tiles per wave
+        constexpr int G = TPW < 4 ? TPW : 4;               // interleave group
+        const __bf16 *qb = bQ(cb), *kb = bK(cb);
+#pragma unroll
+        for (int j0 = 0; j0 < TPW; j0 += G) {
+            int sbv[G], ubv[G];
+            bool live[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                int tix = wi + NP * (j0 + j);
+                live[j] = j0 + j < TPW && tix < NA;
+                if (!live[j]) tix = 0;
+                // tile index -> (Sb, Ub): tix = Ub (Ub + 1) / 2 + Sb
+                int ub = 0;
+#pragma unroll
+                for (int q = 1; q < NU; ++q) ub += tix >= q * (q + 1) / 2 ? 1 : 0;
+                ubv[j] = ub;
+                sbv[j] = tix - ub * (ub + 1) / 2;
+            }
+            f32x4 acc[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 A[KSI][G][NS], Bq[KSI][G][NS];
+#pragma unroll
+            for (int ks = 0; ks < KSI; ++ks) {
+                const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        const __bf16 *kr = kb + (n * C + sbv[j] * 16 + lc) * RS;
+                        const __bf16 *qr = qb + (n * C + ubv[j] * 16 + lc) * RS;
+                        const bf16x4 klo = *(const bf16x4 *)(kr + i_lo);
+                        const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
+                        const bf16x4 khi = i_hi < DK ? *(const bf16x4 *)(kr + i_hi) : zero4();
+                        const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
+                        A[ks][j][n] = cat(klo, khi);
+                        Bq[ks][j][n] = cat(qlo, qhi);
+                    }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSI; ++ks) mma_split_n<NS, G>(A[ks], Bq[ks], acc);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (!live[j]) continue;
+                const int tix = ubv[j] * (ubv[j] + 1) / 2 + sbv[j];
+                const bool diag = sbv[j] == ubv[j];
+                float x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] = (diag && 4 * lg + r > lc) ? 0.f : acc[j][r];   // causal: s <= u
+                unsigned w0[NS], w1[NS];
+                split_pair<NS>(x[0], x[1], w0);
+                split_pair<NS>(x[2], x[3], w1);
+#pragma unroll
+                for (int n = 0; n < NS; ++n)
+                    *(uint2 *)(sA + ((tix * NS + n) * 64 + lane) * 4) = make_uint2(w0[n], w1[n]);
+            }
+        }
+    };
+
     // Pipeline: in iteration it the producers prepare chunk it (LDS buffer
     // it & 1) while the consumers compute chunk it - 1 (LDS buffer
-    // (it - 1) & 1).  The two roles run separate loops with the same barrier
-    // sequence (two per iteration), so each is register-allocated on its own.
+    // (it - 1) & 1).  Phase 1 (up to barrier A): producers issue the loads of
+    // chunk it + 1, take the cumulative decay sums of chunk it and compute the
+    // A^T tiles of chunk it - 1; consumers form S' and V' of chunk it - 1 and
+    // update the state.  Phase 2 (up to barrier B): producers write the scaled
+    // operands of chunk it; consumers compute and store the outputs of chunk
+    // it - 1.  The two roles run separate loops with the same barrier sequence,
+    // so each is register-allocated on its own.
     if (producer) {
         // raw inputs of two chunks (the current one and the next, in flight):
         // a dk column pair, TPG consecutive tokens
         Raw2 rq[2][TPG], rk[2][TPG], rg[2][TPG], rt[2][TPG];
-        auto load_dk = [&](int ch, auto rsel) {
+        auto load_dk = [&](int ch, auto rsel, bool valid) {
             constexpr int R = decltype(rsel)::value;
             const long long t0 = (long long)ch * C;
             const long long base = t0 * row_k;
-            const long long lim = ((T - t0) * H - h) * DK * esz;
+            const long long lim = valid ? ((T - t0) * H - h) * DK * esz : 0;
             const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
             const __amdgpu_buffer_rsrc_t Rg = make_rsrc(gg + base, lim);
             const __amdgpu_buffer_rsrc_t Rt = make_rsrc(gt + base, lim);
-            const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, outputs ? lim : 0);
+            const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, lim);
 #pragma unroll
             for (int m = 0; m < TPG; ++m) {
                 const unsigned o = off_k + m * step_k;
                 rg[R][m] = PR::load(Rg, o);
                 rt[R][m] = PR::load(Rt, o);
                 rk[R][m] = PR::load(Rk, o);
-                rq[R][m] = PR::load(Rq, o);
+                if (outputs) rq[R][m] = PR::load(Rq, o);
             }
         };
         float gam_acc0 = 1.f, gam_acc1 = 1.f;           // products of chunk decays (mode 1)
@@ -366,16 +479,17 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             constexpr int R = decltype(rsel)::value;
             const bool work = prep && it < c_end;
             const int pb = it & 1;
-            // the next chunk's inputs load during this whole iteration
-            if (prep && it + 1 < c_end) load_dk(it + 1, std::integral_constant<int, 1 - R>());
-            // ---- phase 1: local cumulative decay of both columns, in log2 units
+            // the next chunk's inputs load during this whole iteration (past the
+            // last chunk: empty buffer ranges, the loads return zeros)
+            if (prep && it + 1 < c_end) load_dk(it + 1, std::integral_constant<int, 1 - R>(), true);
+            // ---- phase 1: local cumulative sums of g * tau of both columns (nats)
             float cum0[TPG], cum1[TPG];
             if (work) {
                 float run0 = 0.f, run1 = 0.f;
 #pragma unroll
                 for (int m = 0; m < TPG; ++m) {
-                    run0 = __builtin_fmaf(PR::lo(rg[R][m]) * PR::lo(rt[R][m]), -kLog2e, run0);
-                    run1 = __builtin_fmaf(PR::hi(rg[R][m]) * PR::hi(rt[R][m]), -kLog2e, run1);
+                    run0 = PR::gt_lo(rg[R][m], rt[R][m], run0);
+                    run1 = PR::gt_hi(rg[R][m], rt[R][m], run1);
                     cum0[m] = run0;
                     cum1[m] = run1;
                 }
@@ -383,6 +497,9 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                 if (MID / TPG == cgp)
                     *(float2 *)(sMid + c0) = make_float2(cum0[MID % TPG], cum1[MID % TPG]);
             }
+            // A^T tiles of the previous chunk (its operands are complete since
+            // the last barrier)
+            if (outputs && it > c_begin) score_tiles(wave, (it - 1) & 1);
             __syncthreads();                               // barrier A
             // ---- phase 2: gates and scaled operands -> LDS buffer pb
             if (work) {
@@ -396,12 +513,16 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                 }
                 const float2 mid = *(const float2 *)(sMid + c0);
                 bm0 += mid.x; bm1 += mid.y;
-                const float sh0 = off0 - bm0, sh1 = off1 - bm1;
+                // to log2 units: b = -log2(e) * (sum of g * tau)
+                const float sh0 = (bm0 - off0) * kLog2e, sh1 = (bm1 - off1) * kLog2e;
+                bm0 *= -kLog2e; bm1 *= -kLog2e;
+                bL0 *= -kLog2e; bL1 *= -kLog2e;
                 __bf16 *qb = bQ(pb), *kb = bK(pb);
 #pragma unroll
                 for (int m = 0; m < TPG; ++m) {
                     const int u = cgp * TPG + m;
-                    const float d0 = cum0[m] + sh0, d1 = cum1[m] + sh1;          // b_u - b_m
+                    const float d0 = __builtin_fmaf(cum0[m], -kLog2e, sh0);      // b_u - b_m
+                    const float d1 = __builtin_fmaf(cum1[m], -kLog2e, sh1);
                     const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
                     const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
                     unsigned pk[NS];
@@ -429,7 +550,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             }
             __syncthreads();                               // barrier B
         };
-        if (prep && c_begin < c_end) load_dk(c_begin, std::integral_constant<int, 0>());
+        if (prep && c_begin < c_end) load_dk(c_begin, std::integral_constant<int, 0>(), true);
         for (int it = c_begin; it <= c_end; it += 2) {
             iter(it, std::integral_constant<int, 0>());
             if (it + 1 <= c_end) iter(it + 1, std::integral_constant<int, 1>());
@@ -451,10 +572,10 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     u32x4 rvw[LV], rbw[LV];
     Raw rv[KSC][8], rb[KSC][8];
     __bf16 *stg = (__bf16 *)(smem + L::stg_off + (size_t)(producer ? 0 : cw) * L::stg_wave);
-    auto load_v = [&](int ch) {
+    auto load_v = [&](int ch, bool valid) {
         const long long t0 = (long long)ch * C;
         const long long base = t0 * row_v;
-        const long long lim = ((T - t0) * H - h) * dv * esz - (long long)jcol * esz;
+        const long long lim = valid ? ((T - t0) * H - h) * dv * esz - (long long)jcol * esz : 0;
         const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lim);
         const __amdgpu_buffer_rsrc_t Rb = make_rsrc(gb + base, lim);
         if constexpr (kStage) {
@@ -487,13 +608,13 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                 }
         }
     };
-    if (c_begin < c_end) load_v(c_begin);
+    if (c_begin < c_end) load_v(c_begin, true);
 
     for (int it = c_begin; it <= c_end; ++it) {
         const bool cwork = it > c_begin;
         const int cb = (it - 1) & 1;
 
-        // ================= phase 1: S' operands and the A^T tiles of this wave
+        // ================= phase 1: S' and V' operands, state update
         bf16x8 sB[KSI][NS];
         if (cwork && outputs) {
             // B operands S' = diag(exp(b_m)) S_in (k = dk rows)
@@ -512,75 +633,10 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 #pragma unroll
                 for (int n = 0; n < NS; ++n) sB[ks][n] = pack8(w0[n], w1[n], w2[n], w3[n]);
             }
-            // A^T tiles (Sb, Ub), Sb <= Ub (rows s of Kt, columns u of Qt, k = i):
-            // this wave takes tiles cw, cw + NJ, ..., in interleaved groups
-            constexpr int TPW = (NA + NJ - 1) / NJ;            // tiles per wave
-            constexpr int G = TPW < 4 ? TPW : 4;               // interleave group
-            const __bf16 *qb = bQ(cb), *kb = bK(cb);
-#pragma unroll
-            for (int j0 = 0; j0 < TPW; j0 += G) {
-                int sbv[G], ubv[G];
-                bool live[G];
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    int tix = cw + NJ * (j0 + j);
-                    live[j] = j0 + j < TPW && tix < NA;
-                    if (!live[j]) tix = 0;
-                    // tile index -> (Sb, Ub): tix = Ub (Ub + 1) / 2 + Sb
-                    int ub = 0;
-#pragma unroll
-                    for (int q = 1; q < NU; ++q) ub += tix >= q * (q + 1) / 2 ? 1 : 0;
-                    ubv[j] = ub;
-                    sbv[j] = tix - ub * (ub + 1) / 2;
-                }
-                f32x4 acc[G];
-#pragma unroll
-                for (int j = 0; j < G; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                bf16x8 A[KSI][G][NS], Bq[KSI][G][NS];
-#pragma unroll
-                for (int ks = 0; ks < KSI; ++ks) {
-                    const int i_lo = ks * 32 + 4 * lg, i_hi = i_lo + 16;
-#pragma unroll
-                    for (int j = 0; j < G; ++j)
-#pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const __bf16 *kr = kb + (n * C + sbv[j] * 16 + lc) * RS;
-                            const __bf16 *qr = qb + (n * C + ubv[j] * 16 + lc) * RS;
-                            const bf16x4 klo = *(const bf16x4 *)(kr + i_lo);
-                            const bf16x4 qlo = *(const bf16x4 *)(qr + i_lo);
-                            const bf16x4 khi = i_hi < DK ? *(const bf16x4 *)(kr + i_hi) : zero4();
-                            const bf16x4 qhi = i_hi < DK ? *(const bf16x4 *)(qr + i_hi) : zero4();
-                            A[ks][j][n] = cat(klo, khi);
-                            Bq[ks][j][n] = cat(qlo, qhi);
-                        }
-                }
-#pragma unroll
-                for (int ks = 0; ks < KSI; ++ks) mma_split_n<NS, G>(A[ks], Bq[ks], acc);
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    if (!live[j]) continue;
-                    const int tix = ubv[j] * (ubv[j] + 1) / 2 + sbv[j];
-                    const bool diag = sbv[j] == ubv[j];
-                    float x[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        x[r] = (diag && 4 * lg + r > lc) ? 0.f : acc[j][r];   // causal: s <= u
-                    unsigned w0[NS], w1[NS];
-                    split_pair<NS>(x[0], x[1], w0);
-                    split_pair<NS>(x[2], x[3], w1);
-#pragma unroll
-                    for (int n = 0; n < NS; ++n)
-                        *(uint2 *)(sA + ((tix * NS + n) * 64 + lane) * 4) = make_uint2(w0[n], w1[n]);
-                }
-            }
         }
-        __syncthreads();                                   // barrier A
-
-        // ================= phase 2
+        bf16x8 vB[KSC][NS];
         if (cwork) {
-            const long long t0 = (long long)(it - 1) * C;
             // V' = beta_hat * v of this wave's columns, as split B operands (k = tokens)
-            bf16x8 vB[KSC][NS];
             if constexpr (kStage) {
                 // stage this wave's rows, then read them back token-major
 #pragma unroll
@@ -620,7 +676,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                     for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
                 }
             }
-            if (it < c_end) load_v(it);                     // next chunk's v, beta_hat
+            if (it < c_end) load_v(it, true);               // next chunk's v, beta_hat
 
             // dS = diag(exp(b_L - b_m)) Kt^T V' and S = diag(exp(b_L)) S + dS;
             // Kt^T is read with the transposing LDS read (k = tokens).  The NI
@@ -657,7 +713,12 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                     for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[I][r], g0[r] * S[I][r]);
                 }
             }
+        }
+        __syncthreads();                                   // barrier A
 
+        // ================= phase 2: outputs
+        if (cwork) {
+            const long long t0 = (long long)(it - 1) * C;
             if (outputs) {
                 // O = A V' + Qt S' for this wave's columns; the NU token tiles
                 // are independent accumulators, issued interleaved.
@@ -722,7 +783,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const unsigned o = (unsigned)((((long long)(U * 16 + 4 * lg + r)) * row_v + lc) * 4);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[U][r]), Ro, o, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[U][r]), Ro, o, 0, 2);
                     }
             }
         }
@@ -740,15 +801,15 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     }
 }
 
-template <int DK, int DVT, int C, typename TIn>
-hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
+template <int DK, int DVT, int C, typename TIn, bool OUT>
+hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
     typedef Cfg<DK, DVT, C, NS> L;
     const size_t lds = L::bytes;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DK, DVT, C, TIn>,
+        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -767,9 +828,16 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
     a.gam_out = Lc.gam_out;
     const long long blocks = (long long)Lc.B * Lc.H * Lc.n_seg * a.n_jt;
     a.remap = (blocks % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn>), dim3((unsigned)blocks), dim3(L::NT),
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn, OUT>), dim3((unsigned)blocks), dim3(L::NT),
                        lds, stream, a);
     return hipGetLastError();
+}
+
+template <int DK, int DVT, int C, typename TIn>
+hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
+{
+    return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true>(Lc, stream)
+                        : launch_mode<DK, DVT, C, TIn, false>(Lc, stream);
 }
 
 // Instantiates every (DVT, C) tile shape for one dk and defines its size
