@@ -60,9 +60,6 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
             if (seg < 1) seg = 1;
         }
     }
-    if (seg == 1 && dvt > 16 && heads * (dv / dvt) < 160 &&
-        chunk_lds_bytes(dk, dvt / 2, P->C, f32) <= kLdsLimit)
-        dvt /= 2;
     P->DVT = dvt;
     P->lds_bytes = chunk_lds_bytes(dk, dvt, P->C, f32);
     if (P->lds_bytes == 0 || P->lds_bytes > kLdsLimit) return false;

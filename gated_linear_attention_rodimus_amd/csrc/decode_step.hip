@@ -20,6 +20,7 @@ namespace rodimus {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float ld_in(const __bf16 *p, size_t i) { return (float)p[i]; }
@@ -87,7 +88,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
             x.y = a * x.y + kk * v1;
             x.z = a * x.z + kk * v2;
             x.w = a * x.w + kk * v3;
-            S[lt + m * TPP] = x;
+            // streamed back with the non-temporal policy: the next read of this
+            // slice is a whole step (every other layer's state) away
+            __builtin_nontemporal_store(f4v{x.x, x.y, x.z, x.w}, (f4v *)&S[lt + m * TPP]);
             o0 += qi * x.x; o1 += qi * x.y; o2 += qi * x.z; o3 += qi * x.w;
         }
         s_red[slot][rg][4 * c] = o0;
