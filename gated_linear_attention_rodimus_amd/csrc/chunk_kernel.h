@@ -291,7 +291,11 @@ struct Cfg {
     // per consumer wave: raw v and beta_hat of one chunk, [C][16] bf16 each
     static constexpr size_t stg_off = mid_off + (size_t)DK * 4;
     static constexpr size_t stg_wave = (size_t)2 * C * 16 * 2;
-    static constexpr size_t bytes = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
+    // output tile of one chunk, [C][OS] fp32 (row stride DVT + 16 floats: the
+    // four row groups of an MFMA C-layout write land in distinct banks)
+    static constexpr int OS = DVT + 16;
+    static constexpr size_t out_off = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
+    static constexpr size_t bytes = out_off + (size_t)C * OS * 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
@@ -357,7 +361,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     const Raw *gt = (const Raw *)a.tau + head0 * DK;
     const Raw *gv = (const Raw *)a.v + head0 * dv + jcol;
     const Raw *gb = (const Raw *)a.beta + head0 * dv + jcol;
-    float *go = a.out ? a.out + head0 * dv + jcol : nullptr;
+    float *go = a.out ? a.out + head0 * dv + jt * DVT : nullptr;   // this dv tile
 
     // byte offsets of this thread's elements inside one chunk
     const unsigned off_k = (unsigned)(((long long)cgp * TPG * row_k + c0) * esz);
@@ -610,6 +614,26 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     };
     if (c_begin < c_end) load_v(c_begin, true);
 
+    // the block's output tile of chunk ch (staged in LDS by all consumer waves)
+    // to HBM: each wave stores C / NJ whole rows of DVT floats with 16-byte
+    // non-temporal stores; rows past the sequence end are dropped by the range
+    float *sOut = (float *)(smem + L::out_off);
+    auto store_tile = [&](int ch) {
+        constexpr int LPR = DVT / 4;                     // lanes per row
+        constexpr int RPI = 64 / LPR;                    // rows per store
+        constexpr int RPW = C / NJ;                      // rows per consumer wave
+        const long long t0 = (long long)ch * C;
+        const long long lim = ((T - t0) * H - h) * dv * 4 - (long long)jt * DVT * 4;
+        const __amdgpu_buffer_rsrc_t Ro = make_rsrc(go + t0 * row_v, lim);
+        const int col = 4 * (lane % LPR);
+#pragma unroll
+        for (int j = 0; j < RPW / RPI; ++j) {
+            const int u = cw * RPW + j * RPI + lane / LPR;
+            const u32x4 x = *(const u32x4 *)(sOut + u * L::OS + col);
+            __builtin_amdgcn_raw_buffer_store_b128(x, Ro, (unsigned)(((long long)u * row_v + col) * 4), 0, 2);
+        }
+    };
+
     for (int it = c_begin; it <= c_end; ++it) {
         const bool cwork = it > c_begin;
         const int cb = (it - 1) & 1;
@@ -676,6 +700,9 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                     for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
                 }
             }
+            // outputs staged last iteration (issued after the wait for this
+            // chunk's v loads, so that wait does not include these stores)
+            if (outputs && it - 2 >= c_begin) store_tile(it - 2);
             if (it < c_end) load_v(it, true);               // next chunk's v, beta_hat
 
             // dS = diag(exp(b_L - b_m)) Kt^T V' and S = diag(exp(b_L)) S + dS;
@@ -722,8 +749,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             if (outputs) {
                 // O = A V' + Qt S' for this wave's columns; the NU token tiles
                 // are independent accumulators, issued interleaved.
-                const long long lim = ((T - t0) * H - h) * dv * 4 - (long long)jcol * 4;
-                const __amdgpu_buffer_rsrc_t Ro = make_rsrc(go + t0 * row_v, lim);
                 const __bf16 *qb = bQ(cb);
                 f32x4 acc[NU];
 #pragma unroll
@@ -778,17 +803,19 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
                         mma_split_n<NS, NU - 2>(A + 2, Bv + 2, acc + 2);
                     }
                 }
+                // into the block's output tile; stored to HBM as whole rows
+                // after the next barrier
 #pragma unroll
                 for (int U = 0; U < NU; ++U)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const unsigned o = (unsigned)((((long long)(U * 16 + 4 * lg + r)) * row_v + lc) * 4);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[U][r]), Ro, o, 0, 2);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        sOut[(U * 16 + 4 * lg + r) * L::OS + cw * 16 + lc] = acc[U][r];
             }
         }
         __syncthreads();                                   // barrier B
     }
+
+    if (outputs && c_end > c_begin) store_tile(c_end - 1);
 
     // ---- state out
     if (a.s_out && (!a.s_out_last_only || seg == a.n_seg - 1)) {
