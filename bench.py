@@ -12,7 +12,7 @@ batch from the previous step.  After the chunk steps the same run times
 ``--decode-steps`` back-to-back decode steps over 256 x 16 resident fp32
 states (the batched decode workload) and reports the state bandwidth, once on
 one resident state batch (which the 256 MB last-level cache partly holds) and
-once cold, rotating over 12 state batches (402 MB).
+once cold, rotating over 12 state batches (1.6 GB).
 
 One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
 per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
@@ -178,7 +178,7 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
         dbytes, dflops = decode_algorithmic(N, Hd, dkd, dvd)
-        # cold variant: state batches in rotation whose total (12 x 33.5 MB) exceeds
+        # cold variant: state batches in rotation whose total (12 x 134 MB) exceeds
         # the 256 MB last-level cache, as when every layer of a model keeps a state
         n_cold = 12
         Ss = [S] + [S.clone() for _ in range(n_cold - 1)]

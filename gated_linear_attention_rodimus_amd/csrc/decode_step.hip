@@ -57,9 +57,14 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 
     float4 *S = reinterpret_cast<float4 *>(state) + (size_t)(active ? pair : 0) * F4;
     float4 s[PER];
+    // the slice is read once per step: non-temporal loads keep it from
+    // displacing other data in the caches
 #pragma unroll
-    for (int m = 0; m < PER; ++m)
-        s[m] = active ? S[lt + m * TPP] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m = 0; m < PER; ++m) {
+        const f4v y = active ? __builtin_nontemporal_load((const f4v *)&S[lt + m * TPP])
+                             : f4v{0.f, 0.f, 0.f, 0.f};
+        s[m] = make_float4(y[0], y[1], y[2], y[3]);
+    }
 
     // gates for this slice (rows over dk, columns over dv)
     if (active) {
