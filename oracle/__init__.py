@@ -16,11 +16,17 @@ in float64.  The gate formulas follow the Rodimus* digest page
 the dk rows follows the authors' rebuttal page (paperhub.cn), the
 "Efficient Parallelization" bullet (selection only along n).
 
+``bwd`` is the reverse mode of ``fwd`` written out from the same recurrence
+(the adjoint of the state walked from the last token to the first); at g = 0,
+where g^tau has no derivative, its g^tau terms are taken as 0.
+
 Every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` against a brute-force quadratic form, library
 matmuls in the special cases tau = 0 and constant gates, a division-based
 closed form for dk = dv = 1, the g = 0 invariant, linearity and bitwise
-carry-over.
+carry-over; ``bwd`` by ``tests/test_oracle_bwd.py`` against central finite
+differences of ``fwd``, the matmul gradients of the tau = 0 case, dg = 0 at
+tau = 0 and the T = 0 case.
 
 Inputs may be any numpy floating dtype (bf16 inputs arrive as their exact
 float32 upcast); they are converted to float64 exactly before the C call.
@@ -60,6 +66,8 @@ def _load():
         lib.ddts_oracle_fwd.argtypes = [ctypes.c_int] * 5 + [dp] * 9 + [ctypes.c_int]
         lib.ddts_oracle_decode.restype = ctypes.c_int
         lib.ddts_oracle_decode.argtypes = [ctypes.c_int] * 4 + [dp] * 8
+        lib.ddts_oracle_bwd.restype = ctypes.c_int
+        lib.ddts_oracle_bwd.argtypes = [ctypes.c_int] * 5 + [dp] * 16 + [ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -124,6 +132,39 @@ def decode(q, k, v, g, tau, beta_hat, state):
     if rc < 0:
         raise RuntimeError("ddts_oracle_decode failed")
     return out, st
+
+
+def bwd(q, k, v, g, tau, beta_hat, d_out, initial_state=None, d_final_state=None,
+        nthreads=0):
+    """fp64 reverse mode of ``fwd``: gradients of a loss L given dL/do
+    ([B, T, H, dv]) and optionally dL/dS_T ([B, H, dk, dv]).
+
+    Returns a dict with dq, dk, dg, dtau ([B, T, H, dk]), dv, dbeta_hat
+    ([B, T, H, dv]) and d_initial_state ([B, H, dk, dv]), all float64.  At
+    g = 0 the g^tau terms of dg and dtau are taken as 0.
+    """
+    q, k, g, tau, v, beta_hat, d_out = map(_f64, (q, k, g, tau, v, beta_hat, d_out))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    for a in (k, g, tau):
+        assert a.shape == (B, T, H, dk)
+    for a in (beta_hat, d_out):
+        assert a.shape == (B, T, H, dv)
+    s0 = None if initial_state is None else _f64(initial_state)
+    dsf = None if d_final_state is None else _f64(d_final_state)
+    for a in (s0, dsf):
+        assert a is None or a.shape == (B, H, dk, dv)
+    out = {n: np.empty((B, T, H, dk), np.float64) for n in ("dq", "dk", "dg", "dtau")}
+    out.update({n: np.empty((B, T, H, dv), np.float64) for n in ("dv", "dbeta_hat")})
+    out["d_initial_state"] = np.empty((B, H, dk, dv), np.float64)
+    rc = _load().ddts_oracle_bwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(g), _ptr(tau),
+                                 _ptr(v), _ptr(beta_hat), _ptr(s0), _ptr(d_out), _ptr(dsf),
+                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dg"]),
+                                 _ptr(out["dtau"]), _ptr(out["dv"]), _ptr(out["dbeta_hat"]),
+                                 _ptr(out["d_initial_state"]), int(nthreads))
+    if rc < 0:
+        raise RuntimeError("ddts_oracle_bwd failed")
+    return out
 
 
 def rel_to_rms_error(x_hat, x) -> float:
