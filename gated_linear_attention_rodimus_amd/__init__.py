@@ -9,6 +9,8 @@ of the computation runs in the library's HIP kernels; there is no fallback.
     o, S = chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None,
                      output_final_state=False, chunk=0)
     o = decode_step(q, k, v, g, tau, beta_hat, state)       # state updated in place
+    grads = chunk_bwd(q, k, v, g, tau, beta_hat, d_out, initial_state=None,
+                      d_final_state=None)                     # dict of fp32 gradients
 
 Per head:  alpha = exp(-g*tau), alpha_hat = g**tau (over dk),
 S_t = diag(alpha_t) S_{t-1} + (alpha_hat_t*k_t)(beta_hat_t*v_t)^T, o_t = S_t^T q_t
@@ -20,8 +22,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "lib", "RodimusError",
-           "LIB_PATH", "abi_version"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_bytes", "bwd_workspace_bytes",
+           "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librodimus_ddts.so")
 
@@ -61,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_chunk_fwd_ex.argtypes = [i] * 8 + [vp] * 9 + [vp, sz, vp]
         L.rodimus_ddts_decode_step.restype = i
         L.rodimus_ddts_decode_step.argtypes = [i] * 5 + [vp] * 8 + [vp]
+        L.rodimus_ddts_chunk_bwd_workspace_bytes.restype = sz
+        L.rodimus_ddts_chunk_bwd_workspace_bytes.argtypes = [i] * 5
+        L.rodimus_ddts_chunk_bwd.restype = i
+        L.rodimus_ddts_chunk_bwd.argtypes = [i] * 6 + [vp] * 16 + [vp, sz, vp]
         _lib = L
     return _lib
 
@@ -108,6 +114,10 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name}: expected device {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+
+
+def bwd_workspace_bytes(B, T, H, dk, dv) -> int:
+    return int(lib().rodimus_ddts_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
 
 
 def workspace_bytes(B, T, H, dk, dv, chunk=0, segments=0) -> int:
@@ -181,3 +191,44 @@ def decode_step(q, k, v, g, tau, beta_hat, state, out=None):
     if st != OK:
         raise RodimusError(st, "rodimus_ddts_decode_step")
     return out
+
+
+def chunk_bwd(q, k, v, g, tau, beta_hat, d_out, initial_state=None, d_final_state=None,
+              workspace=None):
+    """Gradients of the chunk forward.  Inputs as ``chunk_fwd`` (bf16 or fp32,
+    contiguous, one GPU); d_out [B, T, H, dv] fp32; d_final_state [B, H, dk, dv]
+    fp32 or None.  Returns a dict of fp32 tensors: dq, dk, dg, dtau
+    ([B, T, H, dk]), dv, dbeta_hat ([B, T, H, dv]), d_initial_state
+    ([B, H, dk, dv])."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd runs on the GPU only; inputs must be on a cuda device")
+    dt = q.dtype
+    _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("g", g), ("tau", tau)):
+        _check_tensor(n, t, (B, T, H, dk), dt, dev)
+    for n, t in (("v", v), ("beta_hat", beta_hat)):
+        _check_tensor(n, t, (B, T, H, dv), dt, dev)
+    _check_tensor("d_out", d_out, (B, T, H, dv), torch.float32, dev)
+    for n, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check_tensor(n, t, (B, H, dk, dv), torch.float32, dev)
+    grads = {n: torch.empty(B, T, H, dk, device=dev) for n in ("dq", "dk", "dg", "dtau")}
+    grads.update({n: torch.empty(B, T, H, dv, device=dev) for n in ("dv", "dbeta_hat")})
+    grads["d_initial_state"] = torch.empty(B, H, dk, dv, device=dev)
+    wsb = bwd_workspace_bytes(B, T, H, dk, dv)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib().rodimus_ddts_chunk_bwd(
+        B, T, H, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v),
+        _ptr(beta_hat), _ptr(initial_state), _ptr(d_out), _ptr(d_final_state),
+        _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dg"]), _ptr(grads["dtau"]),
+        _ptr(grads["dv"]), _ptr(grads["dbeta_hat"]), _ptr(grads["d_initial_state"]),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+        _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_chunk_bwd")
+    return grads

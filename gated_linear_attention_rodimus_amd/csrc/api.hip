@@ -271,4 +271,82 @@ rodimus_status rodimus_ddts_decode_step(
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
 }
 
+size_t rodimus_ddts_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv)
+{
+    if (B <= 0 || H <= 0 || T <= 0 || !width_ok(dk) || !width_ok(dv)) return 0;
+    const int C = chunk_bwd_chunk();
+    return (size_t)B * H * ((T + C - 1) / C) * dk * dv * sizeof(float);
+}
+
+rodimus_status rodimus_ddts_chunk_bwd(
+    int B, int T, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const float *initial_state,
+    const float *d_out, const float *d_final_state,
+    float *dq, float *dk_, float *dg, float *dtau, float *dv_, float *dbeta_hat,
+    float *d_initial_state, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    rodimus_status st = check_chunk_args(B, T, H, dk, dv, 0, 0, in_dtype);
+    if (st != RODIMUS_OK) return st;
+    const size_t lds = chunk_bwd_lds_bytes(dk, dv);
+    if (lds == 0 || lds > kLdsLimit) return RODIMUS_ERR_UNSUPPORTED;
+    const bool f32 = in_dtype == RODIMUS_DTYPE_F32;
+    const size_t esz = f32 ? 4 : 2;
+    const size_t ntok = (size_t)B * T * H;
+    const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+    if (T > 0) {
+        const void *ins[7] = {q, k, g, tau, v, beta_hat, d_out};
+        for (const void *p : ins)
+            if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+        float *outs[6] = {dq, dk_, dg, dtau, dv_, dbeta_hat};
+        for (const float *p : outs)
+            if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+    }
+    const void *opt[3] = {initial_state, d_final_state, d_initial_state};
+    for (const void *p : opt)
+        if (p && !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+    // every output overlaps nothing else
+    const Span s_in[9] = {span(q, ntok * dk * esz), span(k, ntok * dk * esz),
+                          span(g, ntok * dk * esz), span(tau, ntok * dk * esz),
+                          span(v, ntok * dv * esz), span(beta_hat, ntok * dv * esz),
+                          span(d_out, ntok * dv * sizeof(float)),
+                          span(initial_state, initial_state ? state_bytes : 0),
+                          span(d_final_state, d_final_state ? state_bytes : 0)};
+    const Span s_out[7] = {span(dq, T > 0 ? ntok * dk * 4 : 0), span(dk_, T > 0 ? ntok * dk * 4 : 0),
+                           span(dg, T > 0 ? ntok * dk * 4 : 0), span(dtau, T > 0 ? ntok * dk * 4 : 0),
+                           span(dv_, T > 0 ? ntok * dv * 4 : 0), span(dbeta_hat, T > 0 ? ntok * dv * 4 : 0),
+                           span(d_initial_state, d_initial_state ? state_bytes : 0)};
+    for (int i = 0; i < 7; ++i) {
+        for (const Span &x : s_in)
+            if (overlap(s_out[i], x)) return RODIMUS_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(s_out[i], s_out[j])) return RODIMUS_ERR_INVALID_ARG;
+    }
+    const size_t wsb = rodimus_ddts_chunk_bwd_workspace_bytes(B, T, H, dk, dv);
+    if (wsb > 0) {
+        if (!workspace || workspace_bytes < wsb) return RODIMUS_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RODIMUS_ERR_INVALID_ARG;
+        const Span s_ws = span(workspace, wsb);
+        for (const Span &x : s_in)
+            if (overlap(s_ws, x)) return RODIMUS_ERR_INVALID_ARG;
+        for (const Span &x : s_out)
+            if (overlap(s_ws, x)) return RODIMUS_ERR_INVALID_ARG;
+    }
+
+    hipError_t e = hipSuccess;
+    if (T == 0) {
+        if (d_initial_state)
+            e = launch_state_copy(d_final_state, d_initial_state, (size_t)B * H * dk * dv, stream);
+        return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+    }
+    ChunkBwdLaunch Lc;
+    Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv; Lc.f32_inputs = f32;
+    Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
+    Lc.s0 = initial_state; Lc.dout = d_out; Lc.dsf = d_final_state;
+    Lc.dq = dq; Lc.dk_ = dk_; Lc.dg = dg; Lc.dtau = dtau; Lc.dv_ = dv_; Lc.dbeta = dbeta_hat;
+    Lc.ds0 = d_initial_state; Lc.ws = (float *)workspace;
+    e = launch_chunk_bwd(Lc, stream);
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
 }  // extern "C"

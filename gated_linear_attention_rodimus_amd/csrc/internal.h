@@ -54,4 +54,18 @@ hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStre
 hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
                          float *state, float *out, hipStream_t stream);
 
+// Backward of the chunk forward (one workgroup per (b, h); a forward sweep
+// stores every chunk-start state in ws, then a backward sweep).
+struct ChunkBwdLaunch {
+    int B, T, H, dk, dv;
+    bool f32_inputs;
+    TokenInputs in;
+    const float *s0, *dout, *dsf;
+    float *dq, *dk_, *dg, *dtau, *dv_, *dbeta, *ds0;
+    float *ws;              // [B*H][ceil(T / chunk)][dk][dv]
+};
+size_t chunk_bwd_lds_bytes(int dk, int dv);   // 0 if the shape is not instantiated
+int chunk_bwd_chunk();                         // tokens per chunk of the backward
+hipError_t launch_chunk_bwd(const ChunkBwdLaunch &L, hipStream_t stream);
+
 }  // namespace rodimus

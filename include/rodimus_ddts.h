@@ -150,6 +150,40 @@ rodimus_status rodimus_ddts_decode_step(
     const void *v, const void *beta_hat,
     float *state, float *out, hipStream_t stream);
 
+/*
+ * Backward of rodimus_ddts_chunk_fwd (the training pass's other half): the
+ * gradients of a loss L with respect to every input of the forward, given
+ * dL/d out and optionally dL/d final_state.  The pages state that training
+ * runs the recurrence chunkwise in parallel (rebuttal page, bullet "Efficient
+ * Parallelization", and the answer on sequential processing bottlenecks);
+ * the gradients are those of the recurrence in the header comment.  At g = 0,
+ * where g^tau has no derivative, its terms in dg and dtau are taken as 0.
+ *
+ *   B, T, H, dk, dv  as rodimus_ddts_chunk_fwd; supported dk x dv: dk <= 64
+ *                    with any dv, dk = 128 with dv <= 32 (else UNSUPPORTED).
+ *   in_dtype, q, k, g, tau, v, beta_hat, initial_state
+ *                    the forward's inputs (initial_state may be NULL = zeros).
+ *   d_out            [B, T, H, dv] fp32, dL/d out.
+ *   d_final_state    [B, H, dk, dv] fp32 or NULL (= zeros).
+ *   dq, dk_, dg, dtau  [B, T, H, dk] fp32 outputs.
+ *   dv_, dbeta_hat   [B, T, H, dv] fp32 outputs.
+ *   d_initial_state  [B, H, dk, dv] fp32 output or NULL.
+ *   workspace        device buffer of rodimus_ddts_chunk_bwd_workspace_bytes
+ *                    (every chunk-start state of the forward, recomputed here).
+ * Outputs must not overlap each other, the inputs or the workspace.
+ * Precision: as the forward (bf16 MFMA products on split operands, fp32
+ * accumulation and state).
+ */
+rodimus_status rodimus_ddts_chunk_bwd(
+    int B, int T, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const float *initial_state,
+    const float *d_out, const float *d_final_state,
+    float *dq, float *dk_, float *dg, float *dtau, float *dv_, float *dbeta_hat,
+    float *d_initial_state, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t rodimus_ddts_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+
 #ifdef __cplusplus
 }
 #endif

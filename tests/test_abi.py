@@ -157,3 +157,53 @@ def test_binding_requires_gpu_tensors():
         R.chunk_fwd(x, x, x, x, x, x)
     with pytest.raises(ValueError):
         R.decode_step(x[0], x[0], x[0], x[0], x[0], x[0], torch.zeros(4, 1, 16, 16))
+
+
+def _bwd(B=1, T=64, H=2, dk=64, dv=128, dtype=R.DTYPE_BF16, ws=None, wsb=0, misalign=None,
+         alias=None, null=None):
+    """rodimus_ddts_chunk_bwd with fake device pointers in argument order:
+    q, k, g, tau, v, beta_hat (0-5), initial_state (6), d_out (7),
+    d_final_state (8), dq, dk, dg, dtau, dv, dbeta_hat (9-14), d_initial_state
+    (15), laid out one after another."""
+    esz = 4 if dtype == R.DTYPE_F32 else 2
+    ntok = B * T * H
+    state = B * H * dk * dv * 4
+    sizes = [ntok * d * esz for d in (dk, dk, dk, dk, dv, dv)] + [state, ntok * dv * 4, state]
+    sizes += [ntok * d * 4 for d in (dk, dk, dk, dk, dv, dv)] + [B * H * dk * dv * 4]   # outputs
+    ptrs, a = [], BASE
+    for s in sizes:
+        ptrs.append(a)
+        a += ((s + MB) // 16) * 16
+    if misalign is not None:
+        ptrs[misalign] += 4
+    if alias is not None:
+        ptrs[alias[0]] = ptrs[alias[1]]
+    if null is not None:
+        ptrs[null] = 0
+    vp = ctypes.c_void_p
+    p = [vp(x) if x else None for x in ptrs]
+    return R.lib().rodimus_ddts_chunk_bwd(B, T, H, dk, dv, dtype, *p, vp(ws) if ws else None, wsb, None)
+
+
+def test_bwd_workspace_bytes():
+    assert R.bwd_workspace_bytes(2, 100, 3, 64, 128) == 2 * 3 * 7 * 64 * 128 * 4    # 16-token chunks
+    assert R.bwd_workspace_bytes(1, 0, 1, 64, 64) == 0
+
+
+def test_bwd_validation():
+    assert _bwd() == R.ERR_WORKSPACE                                       # no workspace
+    assert _bwd(dk=128, dv=128) == R.ERR_UNSUPPORTED                       # LDS does not fit
+    assert _bwd(dk=48) == R.ERR_UNSUPPORTED
+    assert _bwd(dtype=7) == R.ERR_UNSUPPORTED
+    assert _bwd(misalign=0) == R.ERR_INVALID_ARG                           # q misaligned
+    assert _bwd(misalign=9) == R.ERR_INVALID_ARG                           # dq misaligned
+    assert _bwd(null=7) == R.ERR_INVALID_ARG                               # no d_out
+    assert _bwd(null=6) == R.ERR_WORKSPACE                                 # no S0: allowed
+    assert _bwd(null=10) == R.ERR_INVALID_ARG                              # no dk
+    assert _bwd(alias=(9, 0)) == R.ERR_INVALID_ARG                         # dq over q
+    assert _bwd(alias=(10, 9)) == R.ERR_INVALID_ARG                        # dk over dq
+    assert _bwd(alias=(15, 6)) == R.ERR_INVALID_ARG                        # dS0 over S0
+    assert _bwd(alias=(14, 7)) == R.ERR_INVALID_ARG                        # dbeta over d_out
+    assert _bwd(B=0) == R.ERR_INVALID_ARG
+    # workspace overlapping an output
+    assert _bwd(ws=BASE + 16, wsb=1 << 40) == R.ERR_INVALID_ARG
