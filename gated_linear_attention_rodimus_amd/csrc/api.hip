@@ -194,6 +194,7 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
     Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.gam_out = nullptr;
+    Lc.s_chunks = nullptr;
     const long long sz = (long long)dk * dv;
     if (P.segments == 1) {
         Lc.n_seg = 1; Lc.mode = 0;
@@ -275,7 +276,7 @@ size_t rodimus_ddts_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int d
 {
     if (B <= 0 || H <= 0 || T <= 0 || !width_ok(dk) || !width_ok(dv)) return 0;
     const int C = chunk_bwd_chunk();
-    return (size_t)B * H * ((T + C - 1) / C) * dk * dv * sizeof(float);
+    return (size_t)B * H * ((T + C - 1) / C + 1) * dk * dv * sizeof(float);
 }
 
 rodimus_status rodimus_ddts_chunk_bwd(
@@ -339,12 +340,35 @@ rodimus_status rodimus_ddts_chunk_bwd(
             e = launch_state_copy(d_final_state, d_initial_state, (size_t)B * H * dk * dv, stream);
         return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
     }
+    // (1) the forward's state at every chunk start and its final state, from
+    //     one state-only sweep of the chunk kernel at the backward's chunk length
+    const int C = chunk_bwd_chunk();
+    const int n_chunks = (T + C - 1) / C;
+    float *ws_states = (float *)workspace;                                  // [BH][n_chunks][dk][dv]
+    float *ws_final = ws_states + (size_t)B * H * n_chunks * dk * dv;       // [BH][dk][dv]
+    ChunkPlan P;
+    if (!make_plan(B, T, H, dk, dv, C, 1, f32, &P) || P.C != C) return RODIMUS_ERR_UNSUPPORTED;
+    ChunkLaunch F;
+    F.B = B; F.T = T; F.H = H; F.dk = dk; F.dv = dv;
+    F.C = P.C; F.DVT = P.DVT; F.n_seg = 1; F.chunks_per_seg = P.chunks_per_seg;
+    F.mode = 1; F.f32_inputs = f32;
+    F.in = TokenInputs{q, k, g, tau, v, beta_hat};
+    F.s_in = initial_state; F.s_in_bh_stride = (long long)dk * dv; F.s_in_seg_stride = 0;
+    F.out = nullptr;
+    F.s_out = ws_final; F.s_out_bh_stride = (long long)dk * dv; F.s_out_seg_stride = 0;
+    F.s_out_last_only = 0;
+    F.gam_out = nullptr;
+    F.s_chunks = ws_states;
+    e = launch_chunk(F, stream);
+    if (e != hipSuccess) return RODIMUS_ERR_HIP;
+    // (2) the backward sweep
     ChunkBwdLaunch Lc;
     Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv; Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
-    Lc.s0 = initial_state; Lc.dout = d_out; Lc.dsf = d_final_state;
+    Lc.dout = d_out; Lc.dsf = d_final_state;
+    Lc.s_chunks = ws_states; Lc.s_final = ws_final;
     Lc.dq = dq; Lc.dk_ = dk_; Lc.dg = dg; Lc.dtau = dtau; Lc.dv_ = dv_; Lc.dbeta = dbeta_hat;
-    Lc.ds0 = d_initial_state; Lc.ws = (float *)workspace;
+    Lc.ds0 = d_initial_state;
     e = launch_chunk_bwd(Lc, stream);
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
 }

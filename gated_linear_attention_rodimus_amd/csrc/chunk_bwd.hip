@@ -23,11 +23,10 @@
 // depend on lambda_r only through e^{b_u - b_s} with s < r <= u and through e^{b_u},
 // e^{b_L}, which is what the two sums count.
 //
-// One workgroup of 8 waves per (b, h) runs two sweeps:
-//  1. forward over the chunks, storing every chunk-start state (fp32) in the
-//     workspace and ending with the final state in LDS;
-//  2. backward over the chunks with D (dk x dv fp32) in LDS.
-// Chunks are 16 tokens.  Every product is a 16x16-tile MFMA
+// The chunk-start states come from a state-only sweep of the forward chunk
+// kernel at the same 16-token chunk length (in the workspace); this kernel then
+// runs the backward sweep, one workgroup of 8 waves per (b, h), with the state
+// adjoint D (dk x dv fp32) in LDS.  Every product is a 16x16-tile MFMA
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate) whose fp32 LDS operands are split
 // into NS bf16 terms as they are read (NS = 2 for bf16 inputs, 3 for fp32), as in
 // the forward.  Tail tokens read as zero (inert) and their gradients are not stored.
@@ -47,9 +46,10 @@ constexpr int kWaves = kThreads / 64;
 struct BwdArgs {
     int T, H, n_chunks;
     const void *q, *k, *g, *tau, *v, *beta;
-    const float *s0, *dout, *dsf;
+    const float *dout, *dsf;
+    const float *s_chunks;             // [B*H][n_chunks][DK][DV] chunk-start states
+    const float *s_final;              // [B*H][DK][DV]
     float *dq, *dk, *dg, *dtau, *dv, *dbeta, *ds0;
-    float *ws;                         // [B*H][n_chunks][DK][DV]
 };
 
 // LDS layout in floats; rows padded by one float so row- and column-wise
@@ -58,9 +58,12 @@ template <int DK, int DV>
 struct Cfg {
     static constexpr int C = kC;
     static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1;
+    // [C][SK] arrays: q, k, g, tau, Qt, Kt, e^{b-b_m}, e^{b_m-b}, g^tau, q dq, k' dk', d(g^tau)
     static constexpr int o_q = 0, o_k = o_q + C * SK, o_g = o_k + C * SK, o_t = o_g + C * SK;
     static constexpr int o_qt = o_t + C * SK, o_kt = o_qt + C * SK, o_eb = o_kt + C * SK;
-    static constexpr int o_xq = o_eb + C * SK, o_xk = o_xq + C * SK, o_ya = o_xk + C * SK;
+    static constexpr int o_ei = o_eb + C * SK, o_ah = o_ei + C * SK;
+    static constexpr int o_xq = o_ah + C * SK, o_xk = o_xq + C * SK, o_ya = o_xk + C * SK;
+    // [C][SV] arrays: v, beta_hat, V', dO
     static constexpr int o_v = o_ya + C * SK, o_b = o_v + C * SV, o_vp = o_b + C * SV;
     static constexpr int o_do = o_vp + C * SV;
     static constexpr int o_a = o_do + C * SV, o_da = o_a + C * SC;
@@ -68,6 +71,10 @@ struct Cfg {
     static constexpr int o_bm = o_d + DK * SV, o_fl = o_bm + DK, o_el = o_fl + DK, o_rs = o_el + DK;
     static constexpr int floats = o_rs + DK;
     static constexpr size_t bytes = (size_t)floats * 4;
+    // per-thread register prefetch of one chunk
+    static constexpr int PK = (C * DK + kThreads - 1) / kThreads;    // per [C][DK] tensor
+    static constexpr int PV = (C * DV + kThreads - 1) / kThreads;    // per [C][DV] tensor
+    static constexpr int PS = (DK * DV + kThreads - 1) / kThreads;   // of the state
 };
 
 __device__ __forceinline__ float ld_in(const __bf16 *p, size_t i) { return (float)p[i]; }
@@ -126,11 +133,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
     constexpr int SK = L::SK, SV = L::SV, SC = L::SC;
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float *sq = sm + L::o_q, *sk = sm + L::o_k, *sg = sm + L::o_g, *st = sm + L::o_t;
-    float *sQt = sm + L::o_qt, *sKt = sm + L::o_kt, *sEb = sm + L::o_eb;
-    float *sXq = sm + L::o_xq, *sXk = sm + L::o_xk, *sYa = sm + L::o_ya;
+    float *sQt = sm + L::o_qt, *sKt = sm + L::o_kt, *sEb = sm + L::o_eb, *sEi = sm + L::o_ei;
+    float *sAh = sm + L::o_ah, *sXq = sm + L::o_xq, *sXk = sm + L::o_xk, *sYa = sm + L::o_ya;
     float *sv = sm + L::o_v, *sb = sm + L::o_b, *sVp = sm + L::o_vp, *sdO = sm + L::o_do;
     float *sA = sm + L::o_a, *sdA = sm + L::o_da, *sS = sm + L::o_s, *sD = sm + L::o_d;
     float *sbm = sm + L::o_bm, *sfl = sm + L::o_fl, *sel = sm + L::o_el, *srs = sm + L::o_rs;
+    constexpr int PK = L::PK, PV = L::PV, PS = L::PS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,89 +148,64 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
     const long long head0 = (long long)b * T * H + h;
     const TIn *gq = (const TIn *)a.q, *gk = (const TIn *)a.k, *gg = (const TIn *)a.g;
     const TIn *gt = (const TIn *)a.tau, *gv = (const TIn *)a.v, *gb = (const TIn *)a.beta;
-    float *ws = a.ws + (size_t)bh * a.n_chunks * DK * DV;
+    const float *ws = a.s_chunks + (size_t)bh * a.n_chunks * DK * DV;
     const int lc = lane & 15, lg = lane >> 4;
+    auto gidx_k = [&](long long t, int i) { return (size_t)((head0 + t * H) * DK + i); };
+    auto gidx_v = [&](long long t, int j) { return (size_t)((head0 + t * H) * DV + j); };
 
-    // inputs of chunk c into LDS (fp32); tokens past T read as zero
-    auto load_chunk = [&](int c, bool with_q_do) {
+    // one chunk's inputs and chunk-start state, prefetched into registers a
+    // chunk ahead (tokens past T read as zero)
+    float pq[PK], pk[PK], pg[PK], pt[PK], pv[PV], pb[PV], pd[PV], ps[PS];
+    auto prefetch = [&](int c) {
         const long long t0 = (long long)c * C;
-        for (int e = tid; e < C * DK; e += kThreads) {
-            const int u = e / DK, i = e % DK;
-            const bool ok = t0 + u < T;
-            const size_t gi = (size_t)((head0 + (t0 + u) * H) * DK + i);
-            sk[u * SK + i] = ok ? ld_in(gk, gi) : 0.f;
-            sg[u * SK + i] = ok ? ld_in(gg, gi) : 0.f;
-            st[u * SK + i] = ok ? ld_in(gt, gi) : 0.f;
-            if (with_q_do) sq[u * SK + i] = ok ? ld_in(gq, gi) : 0.f;
-        }
-        for (int e = tid; e < C * DV; e += kThreads) {
-            const int u = e / DV, j = e % DV;
-            const bool ok = t0 + u < T;
-            const size_t gi = (size_t)((head0 + (t0 + u) * H) * DV + j);
-            const float vv = ok ? ld_in(gv, gi) : 0.f, bb = ok ? ld_in(gb, gi) : 0.f;
-            sv[u * SV + j] = vv;
-            sb[u * SV + j] = bb;
-            sVp[u * SV + j] = vv * bb;
-            if (with_q_do) sdO[u * SV + j] = ok ? a.dout[gi] : 0.f;
-        }
-    };
-    // per dk column: chunk-local cumulative sum (log2 units) into sEb as
-    // e^{b - b_m}, and e^{b_m}, e^{b_L - b_m}, e^{b_L}
-    auto gates = [&]() {
-        for (int i = tid; i < DK; i += kThreads) {
-            float run = 0.f, bm = 0.f;
-            for (int u = 0; u < C; ++u) {
-                run = __builtin_fmaf(sg[u * SK + i] * st[u * SK + i], -kLog2e, run);
-                sEb[u * SK + i] = run;
-                if (u == C / 2 - 1) bm = run;
-            }
-            for (int u = 0; u < C; ++u) sEb[u * SK + i] = __builtin_amdgcn_exp2f(sEb[u * SK + i] - bm);
-            sbm[i] = __builtin_amdgcn_exp2f(bm);
-            sfl[i] = __builtin_amdgcn_exp2f(run - bm);
-            sel[i] = __builtin_amdgcn_exp2f(run);
-        }
-    };
-
-    // ================= sweep 1: forward, chunk-start states to the workspace
-    for (int e = tid; e < DK * DV; e += kThreads) {
-        const int i = e / DV, j = e % DV;
-        sS[i * SV + j] = a.s0 ? a.s0[(size_t)bh * DK * DV + e] : 0.f;
-    }
-    for (int c = 0; c < a.n_chunks; ++c) {
-        __syncthreads();
-        for (int e = tid; e < DK * DV; e += kThreads) ws[(size_t)c * DK * DV + e] = sS[(e / DV) * SV + e % DV];
-        load_chunk(c, false);
-        __syncthreads();
-        gates();
-        __syncthreads();
-        // Kt = k' e^{b_m - b}
-        for (int e = tid; e < C * DK; e += kThreads) {
-            const int u = e / DK, i = e % DK;
-            sKt[u * SK + i] = gate_pow(sg[u * SK + i], st[u * SK + i]) * sk[u * SK + i] / sEb[u * SK + i];
-        }
-        __syncthreads();
-        // S = diag(e^{b_L}) S + (Kt diag(f))^T V'   (dk x dv tiles, k = tokens)
-        for (int tile = wave; tile < (DK / 16) * (DV / 16); tile += kWaves) {
-            const int I = tile / (DV / 16), J = tile % (DV / 16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mm<NS>(acc, sKt + I * 16, 1, SK, nullptr, sVp + J * 16, SV, 1, C, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = I * 16 + 4 * lg + r, j = J * 16 + lc;
-                sS[i * SV + j] = __builtin_fmaf(sfl[i], acc[r], sel[i] * sS[i * SV + j]);
+        for (int m = 0; m < PK; ++m) {
+            const int e = tid + m * kThreads, u = e / DK, i = e % DK;
+            const bool ok = e < C * DK && t0 + u < T;
+            pq[m] = ok ? ld_in(gq, gidx_k(t0 + u, i)) : 0.f;
+            pk[m] = ok ? ld_in(gk, gidx_k(t0 + u, i)) : 0.f;
+            pg[m] = ok ? ld_in(gg, gidx_k(t0 + u, i)) : 0.f;
+            pt[m] = ok ? ld_in(gt, gidx_k(t0 + u, i)) : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < PV; ++m) {
+            const int e = tid + m * kThreads, u = e / DV, j = e % DV;
+            const bool ok = e < C * DV && t0 + u < T;
+            pv[m] = ok ? ld_in(gv, gidx_v(t0 + u, j)) : 0.f;
+            pb[m] = ok ? ld_in(gb, gidx_v(t0 + u, j)) : 0.f;
+            pd[m] = ok ? a.dout[gidx_v(t0 + u, j)] : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < PS; ++m) {
+            const int e = tid + m * kThreads;
+            ps[m] = e < DK * DV ? ws[(size_t)c * DK * DV + e] : 0.f;
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int m = 0; m < PK; ++m) {
+            const int e = tid + m * kThreads, u = e / DK, i = e % DK;
+            if (e < C * DK) {
+                sq[u * SK + i] = pq[m]; sk[u * SK + i] = pk[m];
+                sg[u * SK + i] = pg[m]; st[u * SK + i] = pt[m];
             }
         }
-    }
-    // sS now holds the final state; D starts from dL/dS_T
-    for (int e = tid; e < DK * DV; e += kThreads) {
-        const int i = e / DV, j = e % DV;
-        sD[i * SV + j] = a.dsf ? a.dsf[(size_t)bh * DK * DV + e] : 0.f;
-    }
-
-    // ================= sweep 2: backward
-    for (int c = a.n_chunks - 1; c >= 0; --c) {
-        __syncthreads();
-        // rowsum(S_o * D): S_o (in sS) is this chunk's end state
+#pragma unroll
+        for (int m = 0; m < PV; ++m) {
+            const int e = tid + m * kThreads, u = e / DV, j = e % DV;
+            if (e < C * DV) {
+                sv[u * SV + j] = pv[m]; sb[u * SV + j] = pb[m];
+                sVp[u * SV + j] = pv[m] * pb[m]; sdO[u * SV + j] = pd[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < PS; ++m) {
+            const int e = tid + m * kThreads;
+            if (e < DK * DV) sS[(e / DV) * SV + e % DV] = ps[m];
+        }
+    };
+    // rowsum(S_o * D) per dk row, S_o and D as they are in LDS
+    auto rowsum = [&]() {
         for (int i = tid / 8; i < DK; i += kThreads / 8) {
             float acc = 0.f;
             for (int j = tid % 8; j < DV; j += 8) acc += sS[i * SV + j] * sD[i * SV + j];
@@ -231,17 +214,51 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
             acc += __shfl_xor(acc, 4, 8);
             if (tid % 8 == 0) srs[i] = acc;
         }
+    };
+
+    // S_T and D = dL/dS_T, and the last chunk's rowsum
+    for (int e = tid; e < DK * DV; e += kThreads) {
+        const int i = e / DV, j = e % DV;
+        sS[i * SV + j] = a.s_final[(size_t)bh * DK * DV + e];
+        sD[i * SV + j] = a.dsf ? a.dsf[(size_t)bh * DK * DV + e] : 0.f;
+    }
+    if (a.n_chunks > 0) prefetch(a.n_chunks - 1);
+    __syncthreads();
+    rowsum();
+
+    for (int c = a.n_chunks - 1; c >= 0; --c) {
+        const long long t0 = (long long)c * C;
         __syncthreads();
-        for (int e = tid; e < DK * DV; e += kThreads) sS[(e / DV) * SV + e % DV] = ws[(size_t)c * DK * DV + e];
-        load_chunk(c, true);
+        stage();                                   // S_in(c) and the inputs of chunk c
+        if (c > 0) prefetch(c - 1);
         __syncthreads();
-        gates();
+        // per dk column: chunk-local cumulative sum of lambda (log2 units), kept in
+        // sEb; e^{b_m}, e^{b_L - b_m}, e^{b_L}
+        for (int i = tid; i < DK; i += kThreads) {
+            float run = 0.f, bm = 0.f;
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                run = __builtin_fmaf(sg[u * SK + i] * st[u * SK + i], -kLog2e, run);
+                sEb[u * SK + i] = run;
+                if (u == C / 2 - 1) bm = run;
+            }
+            sbm[i] = __builtin_amdgcn_exp2f(bm);
+            sfl[i] = __builtin_amdgcn_exp2f(run - bm);
+            sel[i] = __builtin_amdgcn_exp2f(run);
+            sXq[i] = bm;                            // b_m, read back below
+        }
         __syncthreads();
+        // per element: e^{b-b_m}, e^{b_m-b}, g^tau, Qt, Kt
         for (int e = tid; e < C * DK; e += kThreads) {
             const int u = e / DK, i = e % DK;
-            const float eb = sEb[u * SK + i];
+            const float d = sEb[u * SK + i] - sXq[i];
+            const float eb = __builtin_amdgcn_exp2f(d), ei = __builtin_amdgcn_exp2f(-d);
+            const float ah = gate_pow(sg[u * SK + i], st[u * SK + i]);
+            sEb[u * SK + i] = eb;                   // each thread rewrites only its element
+            sEi[u * SK + i] = ei;
+            sAh[u * SK + i] = ah;
             sQt[u * SK + i] = sq[u * SK + i] * eb;
-            sKt[u * SK + i] = gate_pow(sg[u * SK + i], st[u * SK + i]) * sk[u * SK + i] / eb;
+            sKt[u * SK + i] = ah * sk[u * SK + i] * ei;
         }
         __syncthreads();
         // A = tril(Qt Kt^T) and dA = tril(dO V'^T), [u][s]
@@ -252,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
             else acc = tile_mm<NS>(acc, sdO, SV, 1, nullptr, sVp, 1, SV, DV, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int u = 4 * lg + r, s = lc;
-                dst[u * SC + s] = s <= u ? acc[r] : 0.f;
+                const int u = 4 * lg + r, s_ = lc;
+                dst[u * SC + s_] = s_ <= u ? acc[r] : 0.f;
             }
         }
         __syncthreads();
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                     const int u = 4 * lg + r, i = I * 16 + lc;
                     const float dqv = sEb[u * SK + i] * acc[r];
                     sXq[u * SK + i] = sq[u * SK + i] * dqv;
-                    if ((long long)c * C + u < T) a.dq[(size_t)((head0 + ((long long)c * C + u) * H) * DK + i)] = dqv;
+                    if (t0 + u < T) a.dq[gidx_k(t0 + u, i)] = dqv;
                 }
             } else if (tile < 2 * NQ) {            // dKt columns I
                 const int I = tile - NQ;
@@ -285,11 +302,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int u = 4 * lg + r, i = I * 16 + lc;
-                    const float ah = gate_pow(sg[u * SK + i], st[u * SK + i]);
-                    const float dkp = acc[r] / sEb[u * SK + i];          // dL/dk'
+                    const float ah = sAh[u * SK + i];
+                    const float dkp = acc[r] * sEi[u * SK + i];          // dL/dk'
                     sXk[u * SK + i] = ah * sk[u * SK + i] * dkp;
                     sYa[u * SK + i] = sk[u * SK + i] * dkp;             // dL/d(g^tau)
-                    if ((long long)c * C + u < T) a.dk[(size_t)((head0 + ((long long)c * C + u) * H) * DK + i)] = ah * dkp;
+                    if (t0 + u < T) a.dk[gidx_k(t0 + u, i)] = ah * dkp;
                 }
             } else {                               // dV' columns J
                 const int J = tile - 2 * NQ;
@@ -298,16 +315,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int u = 4 * lg + r, j = J * 16 + lc;
-                    if ((long long)c * C + u < T) {
-                        const size_t gi = (size_t)((head0 + ((long long)c * C + u) * H) * DV + j);
-                        a.dv[gi] = sb[u * SV + j] * acc[r];
-                        a.dbeta[gi] = sv[u * SV + j] * acc[r];
+                    if (t0 + u < T) {
+                        a.dv[gidx_v(t0 + u, j)] = sb[u * SV + j] * acc[r];
+                        a.dbeta[gidx_v(t0 + u, j)] = sv[u * SV + j] * acc[r];
                     }
                 }
             }
         }
         __syncthreads();
-        // dL/dS_in = diag(e^{b_L}) D + diag(e^{b_m}) Qt^T dO, into D
+        // dL/dS_in = diag(e^{b_L}) D + diag(e^{b_m}) Qt^T dO, into D; meanwhile the
+        // reverse cumulative sums dlambda = rowsum(S_o D) + sum_{u' >= u} (q dq - k' dk')
         for (int tile = wave; tile < (DK / 16) * (DV / 16); tile += kWaves) {
             const int I = tile / (DV / 16), J = tile % (DV / 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -318,25 +335,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 sD[i * SV + j] = __builtin_fmaf(sbm[i], acc[r], sel[i] * sD[i * SV + j]);
             }
         }
-        // dlambda by reverse cumulative sums per dk column, then dg, dtau
         for (int i = tid; i < DK; i += kThreads) {
             float run = srs[i];
+#pragma unroll
             for (int u = C - 1; u >= 0; --u) {
                 run += sXq[u * SK + i] - sXk[u * SK + i];
-                if ((long long)c * C + u < T) {
-                    const float gv_ = sg[u * SK + i], tv = st[u * SK + i];
-                    const float ah = gate_pow(gv_, tv), dah = sYa[u * SK + i];
-                    float dgv = -tv * run, dtv = -gv_ * run;
-                    if (gv_ > 0.f) {
-                        dgv += tv * ah / gv_ * dah;
-                        dtv += ah * (__builtin_amdgcn_logf(gv_) / kLog2e) * dah;
-                    }
-                    const size_t gi = (size_t)((head0 + ((long long)c * C + u) * H) * DK + i);
-                    a.dg[gi] = dgv;
-                    a.dtau[gi] = dtv;
-                }
+                sXq[u * SK + i] = run;               // dlambda
             }
         }
+        __syncthreads();
+        // dg, dtau per element; the previous chunk's rowsum (S_o(c-1) = S_in(c) in
+        // LDS, D = dL/dS_in(c))
+        for (int e = tid; e < C * DK; e += kThreads) {
+            const int u = e / DK, i = e % DK;
+            if (t0 + u < T) {
+                const float gv_ = sg[u * SK + i], tv = st[u * SK + i];
+                const float ah = sAh[u * SK + i], dah = sYa[u * SK + i], dl = sXq[u * SK + i];
+                float dgv = -tv * dl, dtv = -gv_ * dl;
+                if (gv_ > 0.f) {
+                    dgv += tv * ah * __builtin_amdgcn_rcpf(gv_) * dah;
+                    dtv += ah * (__builtin_amdgcn_logf(gv_) * (1.f / kLog2e)) * dah;
+                }
+                a.dg[gidx_k(t0 + u, i)] = dgv;
+                a.dtau[gidx_k(t0 + u, i)] = dtv;
+            }
+        }
+        rowsum();
     }
     __syncthreads();
     if (a.ds0)
@@ -379,9 +403,9 @@ hipError_t launch_chunk_bwd(const ChunkBwdLaunch &Lc, hipStream_t stream)
     bwd_detail::BwdArgs a;
     a.T = Lc.T; a.H = Lc.H; a.n_chunks = (Lc.T + bwd_detail::kC - 1) / bwd_detail::kC;
     a.q = Lc.in.q; a.k = Lc.in.k; a.g = Lc.in.g; a.tau = Lc.in.tau; a.v = Lc.in.v; a.beta = Lc.in.beta;
-    a.s0 = Lc.s0; a.dout = Lc.dout; a.dsf = Lc.dsf;
+    a.dout = Lc.dout; a.dsf = Lc.dsf; a.s_chunks = Lc.s_chunks; a.s_final = Lc.s_final;
     a.dq = Lc.dq; a.dk = Lc.dk_; a.dg = Lc.dg; a.dtau = Lc.dtau; a.dv = Lc.dv_; a.dbeta = Lc.dbeta;
-    a.ds0 = Lc.ds0; a.ws = Lc.ws;
+    a.ds0 = Lc.ds0;
     const int BH = Lc.B * Lc.H;
 #define RODIMUS_BWD_CASE(XK, XV)                                                              \
     if (Lc.dk == XK && Lc.dv == XV)                                                           \

@@ -39,6 +39,7 @@ struct ChunkLaunch {
     float *out;
     float *s_out; long long s_out_bh_stride, s_out_seg_stride; int s_out_last_only;
     float *gam_out;         // [B*H][n_seg][dk] (mode 1)
+    float *s_chunks;        // [B*H][n_chunks][dk][dv] chunk-start states (one sweep), or null
 };
 hipError_t launch_chunk(const ChunkLaunch &L, hipStream_t stream);
 
@@ -60,9 +61,10 @@ struct ChunkBwdLaunch {
     int B, T, H, dk, dv;
     bool f32_inputs;
     TokenInputs in;
-    const float *s0, *dout, *dsf;
+    const float *dout, *dsf;
+    const float *s_chunks;  // [B*H][ceil(T / chunk)][dk][dv] chunk-start states
+    const float *s_final;   // [B*H][dk][dv] final state
     float *dq, *dk_, *dg, *dtau, *dv_, *dbeta, *ds0;
-    float *ws;              // [B*H][ceil(T / chunk)][dk][dv]
 };
 size_t chunk_bwd_lds_bytes(int dk, int dv);   // 0 if the shape is not instantiated
 int chunk_bwd_chunk();                         // tokens per chunk of the backward

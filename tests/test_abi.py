@@ -186,7 +186,7 @@ def _bwd(B=1, T=64, H=2, dk=64, dv=128, dtype=R.DTYPE_BF16, ws=None, wsb=0, misa
 
 
 def test_bwd_workspace_bytes():
-    assert R.bwd_workspace_bytes(2, 100, 3, 64, 128) == 2 * 3 * 7 * 64 * 128 * 4    # 16-token chunks
+    assert R.bwd_workspace_bytes(2, 100, 3, 64, 128) == 2 * 3 * (7 + 1) * 64 * 128 * 4  # 16-token chunks + S_T
     assert R.bwd_workspace_bytes(1, 0, 1, 64, 64) == 0
 
 
