@@ -71,10 +71,6 @@ struct Cfg {
     static constexpr int o_bm = o_d + DK * SV, o_fl = o_bm + DK, o_el = o_fl + DK, o_rs = o_el + DK;
     static constexpr int floats = o_rs + DK;
     static constexpr size_t bytes = (size_t)floats * 4;
-    // per-thread register prefetch of one chunk
-    static constexpr int PK = (C * DK + kThreads - 1) / kThreads;    // per [C][DK] tensor
-    static constexpr int PV = (C * DV + kThreads - 1) / kThreads;    // per [C][DV] tensor
-    static constexpr int PS = (DK * DV + kThreads - 1) / kThreads;   // of the state
 };
 
 __device__ __forceinline__ float ld_in(const __bf16 *p, size_t i) { return (float)p[i]; }
@@ -138,7 +134,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
     float *sv = sm + L::o_v, *sb = sm + L::o_b, *sVp = sm + L::o_vp, *sdO = sm + L::o_do;
     float *sA = sm + L::o_a, *sdA = sm + L::o_da, *sS = sm + L::o_s, *sD = sm + L::o_d;
     float *sbm = sm + L::o_bm, *sfl = sm + L::o_fl, *sel = sm + L::o_el, *srs = sm + L::o_rs;
-    constexpr int PK = L::PK, PV = L::PV, PS = L::PS;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,54 +149,87 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
     auto gidx_v = [&](long long t, int j) { return (size_t)((head0 + t * H) * DV + j); };
 
     // one chunk's inputs and chunk-start state, prefetched into registers a
-    // chunk ahead (tokens past T read as zero)
-    float pq[PK], pk[PK], pg[PK], pt[PK], pv[PV], pb[PV], pd[PV], ps[PS];
+    // chunk ahead with 16-byte loads (tokens past T read as zero): per-token
+    // tensors as 16-byte pieces of token rows, the state as float4s
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    constexpr int EPV = 16 / (int)sizeof(TIn);                  // elements per piece
+    constexpr int NPK = C * DK / EPV, NPV = C * DV / EPV, NPD = C * DV / 4, NPS = DK * DV / 4;
+    constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
+    constexpr int LD = (NPD + kThreads - 1) / kThreads, LS = (NPS + kThreads - 1) / kThreads;
+    u32x4v rq[LK], rk[LK], rg[LK], rt[LK], rv[LV], rb[LV], rd[LD], rs_[LS];
+    auto ld16 = [&](const void *base, size_t elem, bool ok, size_t esz) {
+        return ok ? *(const u32x4v *)((const char *)base + elem * esz) : u32x4v{0u, 0u, 0u, 0u};
+    };
     auto prefetch = [&](int c) {
         const long long t0 = (long long)c * C;
 #pragma unroll
-        for (int m = 0; m < PK; ++m) {
-            const int e = tid + m * kThreads, u = e / DK, i = e % DK;
-            const bool ok = e < C * DK && t0 + u < T;
-            pq[m] = ok ? ld_in(gq, gidx_k(t0 + u, i)) : 0.f;
-            pk[m] = ok ? ld_in(gk, gidx_k(t0 + u, i)) : 0.f;
-            pg[m] = ok ? ld_in(gg, gidx_k(t0 + u, i)) : 0.f;
-            pt[m] = ok ? ld_in(gt, gidx_k(t0 + u, i)) : 0.f;
+        for (int m = 0; m < LK; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DK / EPV), i = (pidx % (DK / EPV)) * EPV;
+            const bool ok = pidx < NPK && t0 + u < T;
+            rq[m] = ld16(gq, gidx_k(t0 + u, i), ok, sizeof(TIn));
+            rk[m] = ld16(gk, gidx_k(t0 + u, i), ok, sizeof(TIn));
+            rg[m] = ld16(gg, gidx_k(t0 + u, i), ok, sizeof(TIn));
+            rt[m] = ld16(gt, gidx_k(t0 + u, i), ok, sizeof(TIn));
         }
 #pragma unroll
-        for (int m = 0; m < PV; ++m) {
-            const int e = tid + m * kThreads, u = e / DV, j = e % DV;
-            const bool ok = e < C * DV && t0 + u < T;
-            pv[m] = ok ? ld_in(gv, gidx_v(t0 + u, j)) : 0.f;
-            pb[m] = ok ? ld_in(gb, gidx_v(t0 + u, j)) : 0.f;
-            pd[m] = ok ? a.dout[gidx_v(t0 + u, j)] : 0.f;
+        for (int m = 0; m < LV; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DV / EPV), j = (pidx % (DV / EPV)) * EPV;
+            const bool ok = pidx < NPV && t0 + u < T;
+            rv[m] = ld16(gv, gidx_v(t0 + u, j), ok, sizeof(TIn));
+            rb[m] = ld16(gb, gidx_v(t0 + u, j), ok, sizeof(TIn));
         }
 #pragma unroll
-        for (int m = 0; m < PS; ++m) {
-            const int e = tid + m * kThreads;
-            ps[m] = e < DK * DV ? ws[(size_t)c * DK * DV + e] : 0.f;
+        for (int m = 0; m < LD; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DV / 4), j = (pidx % (DV / 4)) * 4;
+            rd[m] = ld16(a.dout, gidx_v(t0 + u, j), pidx < NPD && t0 + u < T, 4);
         }
+#pragma unroll
+        for (int m = 0; m < LS; ++m) {
+            const int pidx = tid + m * kThreads;
+            rs_[m] = ld16(ws, (size_t)c * DK * DV + (size_t)pidx * 4, pidx < NPS, 4);
+        }
+    };
+    // element n of a piece as fp32
+    auto elem = [&](const u32x4v &x, int n) -> float {
+        if constexpr (EPV == 8)
+            return __uint_as_float((n & 1) ? (x[n >> 1] & 0xffff0000u) : (x[n >> 1] << 16));
+        else
+            return __uint_as_float(x[n]);
     };
     auto stage = [&]() {
 #pragma unroll
-        for (int m = 0; m < PK; ++m) {
-            const int e = tid + m * kThreads, u = e / DK, i = e % DK;
-            if (e < C * DK) {
-                sq[u * SK + i] = pq[m]; sk[u * SK + i] = pk[m];
-                sg[u * SK + i] = pg[m]; st[u * SK + i] = pt[m];
-            }
+        for (int m = 0; m < LK; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DK / EPV), i = (pidx % (DK / EPV)) * EPV;
+            if (pidx < NPK)
+#pragma unroll
+                for (int n = 0; n < EPV; ++n) {
+                    sq[u * SK + i + n] = elem(rq[m], n); sk[u * SK + i + n] = elem(rk[m], n);
+                    sg[u * SK + i + n] = elem(rg[m], n); st[u * SK + i + n] = elem(rt[m], n);
+                }
         }
 #pragma unroll
-        for (int m = 0; m < PV; ++m) {
-            const int e = tid + m * kThreads, u = e / DV, j = e % DV;
-            if (e < C * DV) {
-                sv[u * SV + j] = pv[m]; sb[u * SV + j] = pb[m];
-                sVp[u * SV + j] = pv[m] * pb[m]; sdO[u * SV + j] = pd[m];
-            }
+        for (int m = 0; m < LV; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DV / EPV), j = (pidx % (DV / EPV)) * EPV;
+            if (pidx < NPV)
+#pragma unroll
+                for (int n = 0; n < EPV; ++n) {
+                    const float vv = elem(rv[m], n), bb = elem(rb[m], n);
+                    sv[u * SV + j + n] = vv; sb[u * SV + j + n] = bb; sVp[u * SV + j + n] = vv * bb;
+                }
         }
 #pragma unroll
-        for (int m = 0; m < PS; ++m) {
-            const int e = tid + m * kThreads;
-            if (e < DK * DV) sS[(e / DV) * SV + e % DV] = ps[m];
+        for (int m = 0; m < LD; ++m) {
+            const int pidx = tid + m * kThreads, u = pidx / (DV / 4), j = (pidx % (DV / 4)) * 4;
+            if (pidx < NPD)
+#pragma unroll
+                for (int n = 0; n < 4; ++n) sdO[u * SV + j + n] = __uint_as_float(rd[m][n]);
+        }
+#pragma unroll
+        for (int m = 0; m < LS; ++m) {
+            const int pidx = tid + m * kThreads, i = (pidx * 4) / DV, j = (pidx * 4) % DV;
+            if (pidx < NPS)
+#pragma unroll
+                for (int n = 0; n < 4; ++n) sS[i * SV + j + n] = __uint_as_float(rs_[m][n]);
         }
     };
     // rowsum(S_o * D) per dk row, S_o and D as they are in LDS
@@ -232,33 +260,34 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
         stage();                                   // S_in(c) and the inputs of chunk c
         if (c > 0) prefetch(c - 1);
         __syncthreads();
-        // per dk column: chunk-local cumulative sum of lambda (log2 units), kept in
-        // sEb; e^{b_m}, e^{b_L - b_m}, e^{b_L}
-        for (int i = tid; i < DK; i += kThreads) {
-            float run = 0.f, bm = 0.f;
-#pragma unroll
-            for (int u = 0; u < C; ++u) {
-                run = __builtin_fmaf(sg[u * SK + i] * st[u * SK + i], -kLog2e, run);
-                sEb[u * SK + i] = run;
-                if (u == C / 2 - 1) bm = run;
-            }
-            sbm[i] = __builtin_amdgcn_exp2f(bm);
-            sfl[i] = __builtin_amdgcn_exp2f(run - bm);
-            sel[i] = __builtin_amdgcn_exp2f(run);
-            sXq[i] = bm;                            // b_m, read back below
-        }
-        __syncthreads();
-        // per element: e^{b-b_m}, e^{b_m-b}, g^tau, Qt, Kt
+        // gates: the 16 tokens of a dk column sit on 16 consecutive lanes
+        // (element e -> column e / C, token e % C), so the chunk-local
+        // cumulative sum of lambda (log2 units) is a 16-lane scan; then
+        // e^{b-b_m}, e^{b_m-b}, g^tau, Qt, Kt per element, and e^{b_m},
+        // e^{b_L - b_m}, e^{b_L} per column
         for (int e = tid; e < C * DK; e += kThreads) {
-            const int u = e / DK, i = e % DK;
-            const float d = sEb[u * SK + i] - sXq[i];
+            const int i = e / C, u = e % C;
+            const float gv_ = sg[u * SK + i], tv = st[u * SK + i];
+            float b_ = -kLog2e * gv_ * tv;
+#pragma unroll
+            for (int o = 1; o < C; o <<= 1) {
+                const float y = __shfl_up(b_, o, C);
+                if (u >= o) b_ += y;
+            }
+            const float bm = __shfl(b_, C / 2 - 1, C), bL = __shfl(b_, C - 1, C);
+            const float d = b_ - bm;
             const float eb = __builtin_amdgcn_exp2f(d), ei = __builtin_amdgcn_exp2f(-d);
-            const float ah = gate_pow(sg[u * SK + i], st[u * SK + i]);
-            sEb[u * SK + i] = eb;                   // each thread rewrites only its element
+            const float ah = gate_pow(gv_, tv);
+            sEb[u * SK + i] = eb;
             sEi[u * SK + i] = ei;
             sAh[u * SK + i] = ah;
             sQt[u * SK + i] = sq[u * SK + i] * eb;
             sKt[u * SK + i] = ah * sk[u * SK + i] * ei;
+            if (u == 0) {
+                sbm[i] = __builtin_amdgcn_exp2f(bm);
+                sfl[i] = __builtin_amdgcn_exp2f(bL - bm);
+                sel[i] = __builtin_amdgcn_exp2f(bL);
+            }
         }
         __syncthreads();
         // A = tril(Qt Kt^T) and dA = tril(dO V'^T), [u][s]
@@ -323,8 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
             }
         }
         __syncthreads();
-        // dL/dS_in = diag(e^{b_L}) D + diag(e^{b_m}) Qt^T dO, into D; meanwhile the
-        // reverse cumulative sums dlambda = rowsum(S_o D) + sum_{u' >= u} (q dq - k' dk')
+        // dL/dS_in = diag(e^{b_L}) D + diag(e^{b_m}) Qt^T dO, into D
         for (int tile = wave; tile < (DK / 16) * (DV / 16); tile += kWaves) {
             const int I = tile / (DV / 16), J = tile % (DV / 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -335,22 +363,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 sD[i * SV + j] = __builtin_fmaf(sbm[i], acc[r], sel[i] * sD[i * SV + j]);
             }
         }
-        for (int i = tid; i < DK; i += kThreads) {
-            float run = srs[i];
-#pragma unroll
-            for (int u = C - 1; u >= 0; --u) {
-                run += sXq[u * SK + i] - sXk[u * SK + i];
-                sXq[u * SK + i] = run;               // dlambda
-            }
-        }
-        __syncthreads();
-        // dg, dtau per element; the previous chunk's rowsum (S_o(c-1) = S_in(c) in
-        // LDS, D = dL/dS_in(c))
+        // meanwhile dlambda = rowsum(S_o D) + reverse cumulative sum over the
+        // chunk's tokens of q dq - k' dk' (a 16-lane scan per dk column), then
+        // dg, dtau; after the barrier the previous chunk's rowsum (S_o(c-1) =
+        // S_in(c) in LDS, D now dL/dS_in(c))
         for (int e = tid; e < C * DK; e += kThreads) {
-            const int u = e / DK, i = e % DK;
+            const int i = e / C, u = e % C;
+            float dl = sXq[u * SK + i] - sXk[u * SK + i];
+#pragma unroll
+            for (int o = 1; o < C; o <<= 1) {
+                const float y = __shfl_down(dl, o, C);
+                if (u + o < C) dl += y;
+            }
+            dl += srs[i];
             if (t0 + u < T) {
                 const float gv_ = sg[u * SK + i], tv = st[u * SK + i];
-                const float ah = sAh[u * SK + i], dah = sYa[u * SK + i], dl = sXq[u * SK + i];
+                const float ah = sAh[u * SK + i], dah = sYa[u * SK + i];
                 float dgv = -tv * dl, dtv = -gv_ * dl;
                 if (gv_ > 0.f) {
                     dgv += tv * ah * __builtin_amdgcn_rcpf(gv_) * dah;
@@ -360,6 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 a.dtau[gidx_k(t0 + u, i)] = dtv;
             }
         }
+        __syncthreads();
         rowsum();
     }
     __syncthreads();
