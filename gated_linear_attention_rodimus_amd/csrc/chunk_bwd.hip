@@ -27,9 +27,12 @@
 // kernel at the same 16-token chunk length (in the workspace); this kernel then
 // runs the backward sweep, one workgroup of 8 waves per (b, h), with the state
 // adjoint D (dk x dv fp32) in LDS.  Every product is a 16x16-tile MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate) whose fp32 LDS operands are split
-// into NS bf16 terms as they are read (NS = 2 for bf16 inputs, 3 for fp32), as in
-// the forward.  Tail tokens read as zero (inert) and their gradients are not stored.
+// (v_mfma_f32_16x16x32_bf16, or v_mfma_f32_16x16x16_bf16 where the contraction
+// runs over the chunk's 16 tokens; fp32 accumulate) whose fp32 LDS operands are
+// split into NS bf16 terms as they are read (NS = 2 for bf16 inputs, 3 for fp32),
+// as in the forward.  The next chunk's inputs and state are loaded into
+// registers (16-byte loads) while the current one is processed.  Tail tokens
+// read as zero (inert) and their gradients are not stored.
 #include "chunk_kernel.h"
 
 namespace rodimus {
@@ -117,6 +120,42 @@ __device__ __forceinline__ f32x4 tile_mm(f32x4 acc, const float *pa, int sar, in
         split8<NS>(bv, B);
         acc = chunk_detail::mma_split<NS>(A, B, acc);
     }
+    return acc;
+}
+
+// The same for K = 16 exactly (the chunk length) on v_mfma_f32_16x16x16_bf16:
+// lane group g takes k = 4g..4g+3 for both operands.
+template <int NS>
+__device__ __forceinline__ f32x4 tile_mm16(f32x4 acc, const float *pa, int sar, int sak,
+                                           const float *pb, int sbk, int sbc, int lane) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const int rc = lane & 15, g = lane >> 4;
+    float av[4], bv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        av[e] = pa[rc * sar + (4 * g + e) * sak];
+        bv[e] = pb[(4 * g + e) * sbk + rc * sbc];
+    }
+    unsigned wa[2][NS], wb[2][NS];
+    chunk_detail::split_pair<NS>(av[0], av[1], wa[0]);
+    chunk_detail::split_pair<NS>(av[2], av[3], wa[1]);
+    chunk_detail::split_pair<NS>(bv[0], bv[1], wb[0]);
+    chunk_detail::split_pair<NS>(bv[2], bv[3], wb[1]);
+    s4 A[NS], B[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        A[n] = __builtin_bit_cast(s4, uint2{wa[0][n], wa[1][n]});
+        B[n] = __builtin_bit_cast(s4, uint2{wb[0][n], wb[1][n]});
+    }
+    // term products of total order < NS, smallest first
+    if constexpr (NS == 3) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[1], B[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[0], B[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[2], B[0], acc, 0, 0, 0);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[0], B[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[1], B[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A[0], B[0], acc, 0, 0, 0);
     return acc;
 }
 
@@ -313,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 const float sc = sbm[I * 16 + lc];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] *= sc;
-                acc = tile_mm<NS>(acc, sdA, SC, 1, nullptr, sKt + I * 16, SK, 1, C, lane);
+                acc = tile_mm16<NS>(acc, sdA, SC, 1, sKt + I * 16, SK, 1, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int u = 4 * lg + r, i = I * 16 + lc;
@@ -327,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 const float sc = sfl[I * 16 + lc];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] *= sc;
-                acc = tile_mm<NS>(acc, sdA, 1, SC, nullptr, sQt + I * 16, SK, 1, C, lane);
+                acc = tile_mm16<NS>(acc, sdA, 1, SC, sQt + I * 16, SK, 1, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int u = 4 * lg + r, i = I * 16 + lc;
@@ -339,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
                 }
             } else {                               // dV' columns J
                 const int J = tile - 2 * NQ;
-                acc = tile_mm<NS>(acc, sA, 1, SC, nullptr, sdO + J * 16, SV, 1, C, lane);
+                acc = tile_mm16<NS>(acc, sA, 1, SC, sdO + J * 16, SV, 1, lane);
                 acc = tile_mm<NS>(acc, sKt, SK, 1, sfl, sD + J * 16, SV, 1, DK, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -356,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bwd_kernel(BwdArgs a)
         for (int tile = wave; tile < (DK / 16) * (DV / 16); tile += kWaves) {
             const int I = tile / (DV / 16), J = tile % (DV / 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = tile_mm<NS>(acc, sQt + I * 16, 1, SK, nullptr, sdO + J * 16, SV, 1, C, lane);
+            acc = tile_mm16<NS>(acc, sQt + I * 16, 1, SK, sdO + J * 16, SV, 1, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = I * 16 + 4 * lg + r, j = J * 16 + lc;
