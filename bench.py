@@ -16,8 +16,9 @@ once cold, rotating over 12 state batches (1.6 GB).
 
 One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
 per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
-launch / its HIP-event-timed duration), the decode-step bandwidth, and the
-fp64 CPU oracle timed on this host on the same workload (a reported baseline).
+launch / its HIP-event-timed duration), the decode-step bandwidth, the
+backward (rodimus_ddts_chunk_bwd) on the same batch, and the fp64 CPU oracle
+timed on this host on the same workload (a reported baseline).
 """
 from __future__ import annotations
 
@@ -73,6 +74,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled over steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--bwd-steps", type=int, default=5, help="timed backward calls (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="layer130m")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -201,6 +203,34 @@ def main():
                   "cold_frac_hbm": round(dbytes / us_cold / 1e3 / HBM_PEAK_GBPS, 4),
                   "tokens_per_s": round(N / (us * 1e-6), 1)}
 
+    # ---------------- backward of the chunk forward on the same batch
+    backward = None
+    if args.bwd_steps > 0:
+        rng = np.random.default_rng(2)
+        d_out = torch.from_numpy(rng.standard_normal((B, T, H, dv), dtype=np.float32)).to(dev)
+        bwsb = R.bwd_workspace_bytes(B, T, H, dk, dv)
+        bws = torch.empty(max(bwsb, 1), dtype=torch.uint8, device=dev)
+        t0_, s0_ = sets[0][0], sets[0][1]
+        for _ in range(2):
+            R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.bwd_steps):
+            R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bus = e0.elapsed_time(e1) * 1e3 / args.bwd_steps
+        ntok = B * T * H
+        bbytes = ntok * ((4 * dk + 2 * dv) * 2 + 4 * dv + (4 * dk + 2 * dv) * 4)
+        backward = {"entry": "rodimus_ddts_chunk_bwd (state sweep + backward sweep)",
+                    "workload": args.workload, "calls": args.bwd_steps,
+                    "us_per_call": round(bus, 1), "tokens_per_s": round(B * T / (bus * 1e-6), 1),
+                    "algorithmic_bytes_per_call": bbytes,
+                    "algorithmic_GBps": round(bbytes / bus / 1e3, 1),
+                    "frac_hbm": round(bbytes / bus / 1e3 / HBM_PEAK_GBPS, 4),
+                    "workspace_bytes": bwsb}
+
     # ---------------- CPU baseline: the fp64 oracle on this host, same workload
     cpu = None
     parity = None
@@ -230,7 +260,8 @@ def main():
                                    f"bf16 inputs, fp32 out/state, chunk {C}",
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
                        "rotating_input_sets": len(sets), "parallelism": "single GPU"},
-            "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "parity": parity}
+            "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "backward": backward,
+            "parity": parity}
     print(json.dumps(line), flush=True)
 
 
