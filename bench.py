@@ -17,7 +17,8 @@ once cold, rotating over 12 state batches (1.6 GB).
 One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
 per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
 launch / its HIP-event-timed duration), the decode-step bandwidth, the
-backward (rodimus_ddts_chunk_bwd) on the same batch, and the fp64 CPU oracle
+backward (rodimus_ddts_chunk_bwd) on the same batch, a 24K-token prefill
+followed by decode steps from its carried state, and the fp64 CPU oracle
 timed on this host on the same workload (a reported baseline).
 """
 from __future__ import annotations
@@ -75,6 +76,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled over steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--bwd-steps", type=int, default=5, help="timed backward calls (0: skip)")
+    ap.add_argument("--serve-steps", type=int, default=100,
+                    help="decode steps after a long prefill (0: skip)")
+    ap.add_argument("--serve-prefill", type=int, default=24576)
+    ap.add_argument("--serve-batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="layer130m")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -231,6 +236,40 @@ def main():
                     "frac_hbm": round(bbytes / bus / 1e3 / HBM_PEAK_GBPS, 4),
                     "workspace_bytes": bwsb}
 
+    # ---------------- prefill then batched decode from the carried state
+    serving = None
+    if args.serve_steps > 0:
+        sx = D.make("decode_batch", B=args.serve_batch, T=args.serve_prefill + 1, H=16)
+        st_ = [sx.torch(n, dev) for n in NAMES]
+        pre = [a[:, :args.serve_prefill].contiguous() for a in st_]
+        tok = [a[:, args.serve_prefill].contiguous() for a in st_]
+        s0 = torch.from_numpy(sx.initial_state).to(dev)
+        Bs, Hs = sx.wl.B, sx.wl.H
+        o_pre = torch.empty(Bs, args.serve_prefill, Hs, sx.wl.dv, device=dev)
+        Sst = torch.empty(Bs, Hs, sx.wl.dk, sx.wl.dv, device=dev)
+        o_dec = torch.empty(Bs, Hs, sx.wl.dv, device=dev)
+        swsb = R.workspace_bytes(Bs, args.serve_prefill, Hs, sx.wl.dk, sx.wl.dv)
+        sws = torch.empty(max(swsb, 1), dtype=torch.uint8, device=dev) if swsb else None
+        R.chunk_fwd(*pre, initial_state=s0, out=o_pre, final_state=Sst, workspace=sws)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        R.chunk_fwd(*pre, initial_state=s0, out=o_pre, final_state=Sst, workspace=sws)
+        e1.record(stream)
+        for _ in range(args.serve_steps):
+            R.decode_step(*tok, Sst, out=o_dec)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = e0.elapsed_time(e1)
+        dec_us = e1.elapsed_time(e2) * 1e3 / args.serve_steps
+        serving = {"workload": f"prefill {args.serve_prefill} tokens x {Bs} sequences x {Hs} heads "
+                               f"(dk {sx.wl.dk}, dv {sx.wl.dv}, bf16), then {args.serve_steps} decode "
+                               "steps from the carried state",
+                   "prefill_ms": round(pre_ms, 3),
+                   "prefill_tokens_per_s": round(Bs * args.serve_prefill / (pre_ms * 1e-3), 1),
+                   "decode_us_per_step": round(dec_us, 2),
+                   "decode_tokens_per_s": round(Bs / (dec_us * 1e-6), 1)}
+
     # ---------------- CPU baseline: the fp64 oracle on this host, same workload
     cpu = None
     parity = None
@@ -261,7 +300,7 @@ def main():
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
                        "rotating_input_sets": len(sets), "parallelism": "single GPU"},
             "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "backward": backward,
-            "parity": parity}
+            "serving": serving, "parity": parity}
     print(json.dumps(line), flush=True)
 
 
