@@ -275,8 +275,8 @@ rodimus_status rodimus_ddts_decode_step(
 size_t rodimus_ddts_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv)
 {
     if (B <= 0 || H <= 0 || T <= 0 || !width_ok(dk) || !width_ok(dv)) return 0;
-    const int C = chunk_bwd_chunk();
-    return (size_t)B * H * ((T + C - 1) / C + 1) * dk * dv * sizeof(float);
+    const int C = chunk_bwd_chunk(dk);
+    return (size_t)B * H * (2 * ((T + C - 1) / C) + 1) * dk * dv * sizeof(float);
 }
 
 rodimus_status rodimus_ddts_chunk_bwd(
@@ -342,10 +342,12 @@ rodimus_status rodimus_ddts_chunk_bwd(
     }
     // (1) the forward's state at every chunk start and its final state, from
     //     one state-only sweep of the chunk kernel at the backward's chunk length
-    const int C = chunk_bwd_chunk();
+    const int C = chunk_bwd_chunk(dk);
     const int n_chunks = (T + C - 1) / C;
+    const size_t sd = (size_t)dk * dv;
     float *ws_states = (float *)workspace;                                  // [BH][n_chunks][dk][dv]
-    float *ws_final = ws_states + (size_t)B * H * n_chunks * dk * dv;       // [BH][dk][dv]
+    float *ws_final = ws_states + (size_t)B * H * n_chunks * sd;            // [BH][dk][dv]
+    float *ws_adj = ws_final + (size_t)B * H * sd;                          // [BH][n_chunks][dk][dv]
     ChunkPlan P;
     if (!make_plan(B, T, H, dk, dv, C, 1, f32, &P) || P.C != C) return RODIMUS_ERR_UNSUPPORTED;
     ChunkLaunch F;
@@ -353,20 +355,20 @@ rodimus_status rodimus_ddts_chunk_bwd(
     F.C = P.C; F.DVT = P.DVT; F.n_seg = 1; F.chunks_per_seg = P.chunks_per_seg;
     F.mode = 1; F.f32_inputs = f32;
     F.in = TokenInputs{q, k, g, tau, v, beta_hat};
-    F.s_in = initial_state; F.s_in_bh_stride = (long long)dk * dv; F.s_in_seg_stride = 0;
+    F.s_in = initial_state; F.s_in_bh_stride = (long long)sd; F.s_in_seg_stride = 0;
     F.out = nullptr;
-    F.s_out = ws_final; F.s_out_bh_stride = (long long)dk * dv; F.s_out_seg_stride = 0;
+    F.s_out = ws_final; F.s_out_bh_stride = (long long)sd; F.s_out_seg_stride = 0;
     F.s_out_last_only = 0;
     F.gam_out = nullptr;
     F.s_chunks = ws_states;
     e = launch_chunk(F, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
-    // (2) the backward sweep
+    // (2) the state adjoint leaving every chunk and (3) the chunk gradients
     ChunkBwdLaunch Lc;
     Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv; Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.dout = d_out; Lc.dsf = d_final_state;
-    Lc.s_chunks = ws_states; Lc.s_final = ws_final;
+    Lc.s_chunks = ws_states; Lc.s_final = ws_final; Lc.d_chunks = ws_adj;
     Lc.dq = dq; Lc.dk_ = dk_; Lc.dg = dg; Lc.dtau = dtau; Lc.dv_ = dv_; Lc.dbeta = dbeta_hat;
     Lc.ds0 = d_initial_state;
     e = launch_chunk_bwd(Lc, stream);

@@ -55,8 +55,10 @@ hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStre
 hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
                          float *state, float *out, hipStream_t stream);
 
-// Backward of the chunk forward (one workgroup per (b, h); a forward sweep
-// stores every chunk-start state in ws, then a backward sweep).
+// Backward of the chunk forward: given the forward's state entering every
+// chunk (a state-only forward sweep at the same chunk length), one adjoint
+// sweep writes dL/dS leaving every chunk and dL/dS_0, then one workgroup per
+// (b, h, chunk) forms the chunk's gradients.
 struct ChunkBwdLaunch {
     int B, T, H, dk, dv;
     bool f32_inputs;
@@ -64,10 +66,11 @@ struct ChunkBwdLaunch {
     const float *dout, *dsf;
     const float *s_chunks;  // [B*H][ceil(T / chunk)][dk][dv] chunk-start states
     const float *s_final;   // [B*H][dk][dv] final state
+    float *d_chunks;        // [B*H][ceil(T / chunk)][dk][dv] dL/dS leaving every chunk (written)
     float *dq, *dk_, *dg, *dtau, *dv_, *dbeta, *ds0;
 };
 size_t chunk_bwd_lds_bytes(int dk, int dv);   // 0 if the shape is not instantiated
-int chunk_bwd_chunk();                         // tokens per chunk of the backward
+int chunk_bwd_chunk(int dk);                   // tokens per chunk of the backward
 hipError_t launch_chunk_bwd(const ChunkBwdLaunch &L, hipStream_t stream);
 
 }  // namespace rodimus

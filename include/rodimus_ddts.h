@@ -159,8 +159,7 @@ rodimus_status rodimus_ddts_decode_step(
  * the gradients are those of the recurrence in the header comment.  At g = 0,
  * where g^tau has no derivative, its terms in dg and dtau are taken as 0.
  *
- *   B, T, H, dk, dv  as rodimus_ddts_chunk_fwd; supported dk x dv: dk <= 64
- *                    with any dv, dk = 128 with dv <= 32 (else UNSUPPORTED).
+ *   B, T, H, dk, dv  as rodimus_ddts_chunk_fwd (every dk, dv in {16, 32, 64, 128}).
  *   in_dtype, q, k, g, tau, v, beta_hat, initial_state
  *                    the forward's inputs (initial_state may be NULL = zeros).
  *   d_out            [B, T, H, dv] fp32, dL/d out.
@@ -168,8 +167,10 @@ rodimus_status rodimus_ddts_decode_step(
  *   dq, dk_, dg, dtau  [B, T, H, dk] fp32 outputs.
  *   dv_, dbeta_hat   [B, T, H, dv] fp32 outputs.
  *   d_initial_state  [B, H, dk, dv] fp32 output or NULL.
- *   workspace        device buffer of rodimus_ddts_chunk_bwd_workspace_bytes
- *                    (every chunk-start state of the forward, recomputed here).
+ *   workspace        device buffer of rodimus_ddts_chunk_bwd_workspace_bytes:
+ *                    the forward's state entering every chunk (64 tokens; 32 at
+ *                    dk = 128), its final state, and dL/dS leaving every chunk,
+ *                    all recomputed here.
  * Outputs must not overlap each other, the inputs or the workspace.
  * Precision: as the forward (bf16 MFMA products on split operands, fp32
  * accumulation and state).

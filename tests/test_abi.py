@@ -186,13 +186,16 @@ def _bwd(B=1, T=64, H=2, dk=64, dv=128, dtype=R.DTYPE_BF16, ws=None, wsb=0, misa
 
 
 def test_bwd_workspace_bytes():
-    assert R.bwd_workspace_bytes(2, 100, 3, 64, 128) == 2 * 3 * (7 + 1) * 64 * 128 * 4  # 16-token chunks + S_T
+    # the state entering and the adjoint leaving every 64-token chunk, and S_T
+    assert R.bwd_workspace_bytes(2, 100, 3, 64, 128) == 2 * 3 * (2 * 2 + 1) * 64 * 128 * 4
+    # 32-token chunks at dk = 128
+    assert R.bwd_workspace_bytes(1, 100, 2, 128, 64) == 1 * 2 * (2 * 4 + 1) * 128 * 64 * 4
     assert R.bwd_workspace_bytes(1, 0, 1, 64, 64) == 0
 
 
 def test_bwd_validation():
     assert _bwd() == R.ERR_WORKSPACE                                       # no workspace
-    assert _bwd(dk=128, dv=128) == R.ERR_UNSUPPORTED                       # LDS does not fit
+    assert _bwd(dk=128, dv=128) == R.ERR_WORKSPACE                         # supported shape
     assert _bwd(dk=48) == R.ERR_UNSUPPORTED
     assert _bwd(dtype=7) == R.ERR_UNSUPPORTED
     assert _bwd(misalign=0) == R.ERR_INVALID_ARG                           # q misaligned

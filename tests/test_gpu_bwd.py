@@ -66,7 +66,7 @@ def check(R, dev, x, d_out, d_sf, s0, bar, heads=None):
     return errs
 
 
-@pytest.mark.parametrize("T", [64, 37, 16, 1])
+@pytest.mark.parametrize("T", [64, 37, 16, 1, 65, 200])
 def test_bwd_tiny_fp32(R, dev, T):
     x = D.make("tiny", T=T)
     rng = np.random.default_rng(5)
@@ -75,15 +75,17 @@ def test_bwd_tiny_fp32(R, dev, T):
     check(R, dev, x, d_out, d_sf, s0, BAR["f32"])
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (64, 128), (128, 16), (128, 32)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 128), (32, 64), (64, 16), (64, 32), (64, 128),
+                                   (128, 16), (128, 32), (128, 64), (128, 128)])
 def test_bwd_widths_bf16(R, dev, dk, dv):
     x = D.make("layer1p6b", B=2, T=93, H=3, dk=dk, dv=dv)
     d_out, d_sf = cotangents(x, 8)
     check(R, dev, x, d_out, d_sf, None, BAR["bf16"])
 
 
-def test_bwd_fp32_widths(R, dev):
-    x = D.make("tiny", B=2, T=70, H=2, dk=64, dv=128)
+@pytest.mark.parametrize("dk,dv,T", [(64, 128, 70), (128, 128, 70), (32, 16, 130)])
+def test_bwd_fp32_widths(R, dev, dk, dv, T):
+    x = D.make("tiny", B=2, T=T, H=2, dk=dk, dv=dv)
     d_out, d_sf = cotangents(x, 9)
     check(R, dev, x, d_out, d_sf, None, BAR["f32"])
 
