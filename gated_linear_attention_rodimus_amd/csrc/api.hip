@@ -289,7 +289,7 @@ rodimus_status rodimus_ddts_chunk_bwd(
 {
     rodimus_status st = check_chunk_args(B, T, H, dk, dv, 0, 0, in_dtype);
     if (st != RODIMUS_OK) return st;
-    const size_t lds = chunk_bwd_lds_bytes(dk, dv);
+    const size_t lds = chunk_bwd_lds_bytes(dk, dv, in_dtype == RODIMUS_DTYPE_F32);
     if (lds == 0 || lds > kLdsLimit) return RODIMUS_ERR_UNSUPPORTED;
     const bool f32 = in_dtype == RODIMUS_DTYPE_F32;
     const size_t esz = f32 ? 4 : 2;
@@ -340,34 +340,17 @@ rodimus_status rodimus_ddts_chunk_bwd(
             e = launch_state_copy(d_final_state, d_initial_state, (size_t)B * H * dk * dv, stream);
         return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
     }
-    // (1) the forward's state at every chunk start and its final state, from
-    //     one state-only sweep of the chunk kernel at the backward's chunk length
+    // workspace: the state entering every chunk, S_T, dL/dS leaving every chunk
     const int C = chunk_bwd_chunk(dk);
     const int n_chunks = (T + C - 1) / C;
     const size_t sd = (size_t)dk * dv;
     float *ws_states = (float *)workspace;                                  // [BH][n_chunks][dk][dv]
     float *ws_final = ws_states + (size_t)B * H * n_chunks * sd;            // [BH][dk][dv]
     float *ws_adj = ws_final + (size_t)B * H * sd;                          // [BH][n_chunks][dk][dv]
-    ChunkPlan P;
-    if (!make_plan(B, T, H, dk, dv, C, 1, f32, &P) || P.C != C) return RODIMUS_ERR_UNSUPPORTED;
-    ChunkLaunch F;
-    F.B = B; F.T = T; F.H = H; F.dk = dk; F.dv = dv;
-    F.C = P.C; F.DVT = P.DVT; F.n_seg = 1; F.chunks_per_seg = P.chunks_per_seg;
-    F.mode = 1; F.f32_inputs = f32;
-    F.in = TokenInputs{q, k, g, tau, v, beta_hat};
-    F.s_in = initial_state; F.s_in_bh_stride = (long long)sd; F.s_in_seg_stride = 0;
-    F.out = nullptr;
-    F.s_out = ws_final; F.s_out_bh_stride = (long long)sd; F.s_out_seg_stride = 0;
-    F.s_out_last_only = 0;
-    F.gam_out = nullptr;
-    F.s_chunks = ws_states;
-    e = launch_chunk(F, stream);
-    if (e != hipSuccess) return RODIMUS_ERR_HIP;
-    // (2) the state adjoint leaving every chunk and (3) the chunk gradients
     ChunkBwdLaunch Lc;
     Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv; Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
-    Lc.dout = d_out; Lc.dsf = d_final_state;
+    Lc.s0 = initial_state; Lc.dout = d_out; Lc.dsf = d_final_state;
     Lc.s_chunks = ws_states; Lc.s_final = ws_final; Lc.d_chunks = ws_adj;
     Lc.dq = dq; Lc.dk_ = dk_; Lc.dg = dg; Lc.dtau = dtau; Lc.dv_ = dv_; Lc.dbeta = dbeta_hat;
     Lc.ds0 = d_initial_state;

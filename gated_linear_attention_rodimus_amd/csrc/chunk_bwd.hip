@@ -113,131 +113,182 @@ __device__ __forceinline__ void op_cols(const float *p, int pitch, int col, int 
         x[e] = (K >= 32 || e < 4) ? p[(size_t)(k0 + kslot(lg, e)) * pitch + col] : 0.f;
 }
 
-// ------------------------------------------------------------------ (2) adjoint sweep
+// ------------------------------------------------------------------ (1, 2) state sweeps
 
 struct SweepArgs {
     int T, H, dv, n_chunks;
-    const void *q, *g, *tau;
-    const float *dout, *dsf;
+    const void *q, *k, *g, *tau, *v, *beta;
+    const float *s0;           // [B*H][DK][dv] initial state or null (zeros)
+    const float *dout, *dsf;   // dL/d out, dL/dS_T (or null)
+    float *s_chunks;           // [B*H][n_chunks][DK][dv]: S entering every chunk
+    float *s_final;            // [B*H][DK][dv]: S_T
     float *d_chunks;           // [B*H][n_chunks][DK][dv]: D = dL/dS leaving every chunk
     float *ds0;                // [B*H][DK][dv] or null
 };
 
-// One workgroup per (b, h, JT columns of dv); wave w owns dk rows 16w..16w+15.
-// D lives in registers in the MFMA C-layout (row 16 w + 4 lg + i, column
-// 16 jt + lc).  Per chunk, last to first: store D (= dL/dS leaving the chunk),
-// then D <- diag(e^{b_L}) D + (q e^{b})^T dO, with q e^{b} (b <= 0, from the
-// chunk start) formed in the A-operand layout directly: lane (lc, lg) holds
-// column r = 16 w + lc at tokens 16 t + 4 lg + i, which for t = 2 ks, 2 ks + 1
-// are the k-slots of step ks.  dO of the chunk is staged in LDS (two buffers)
-// and the next chunk's gates and dO are loaded into registers meanwhile.
-template <int DK, int JT, typename TIn>
-__global__ __launch_bounds__(64 * (DK / 16)) void adjoint_sweep_kernel(SweepArgs a)
+// The two sequential parts, one the mirror of the other, for one (b, h) and JT
+// columns of dv; wave w owns dk rows 16w..16w+15.  The state X lives in
+// registers in the MFMA C-layout (row 16 w + 4 lg + i, column 16 jt + lc).
+//   forward (REV = false), chunks first to last:  store X = S entering the
+//     chunk, then S <- diag(e^{b_L}) S + (k' e^{b_L - b})^T V';
+//   reverse (REV = true), chunks last to first:  store X = D leaving the
+//     chunk, then D <- diag(e^{b_L}) D + (q e^{b})^T dO;
+// with b the chunk's inclusive cumulative sum of -g tau, so both factors are
+// at most 1 in size.  The token-side factor is formed in the A-operand layout
+// directly: lane (lc, lg) holds column r = 16 w + lc at tokens 16 t + 4 lg + i,
+// which for t = 2 ks, 2 ks + 1 are the k-slots of step ks.  The other operand
+// (V' or dO) is staged in LDS, two buffers.  The next chunk's inputs are loaded
+// into the other of two register sets (the loop is unrolled by two, so no
+// register copies wait on them) while the current chunk is processed.
+template <int DK, int JT, typename TIn, bool REV>
+__device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
     constexpr int C = ChunkOf<DK>::C, NU = C / 16, NW = DK / 16, NT = 64 * NW;
     constexpr int NJ = JT / 16, PJ = JT + 4;
-    constexpr int NPD = C * JT / 4, LD = (NPD + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) float sdo[2][C * PJ];
+    typedef typename std::conditional<REV, float, TIn>::type TB;   // staged operand input type
+    constexpr int EPB = 16 / (int)sizeof(TB), NPB = C * JT / EPB, LB = (NPB + NT - 1) / NT;
+    typedef typename chunk_detail::InRaw<TIn>::type Raw;
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    struct Regs {
+        Raw x[NU][4], g[NU][4], t[NU][4];
+        u32x4v b0[LB], b1[REV ? 1 : LB];
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x, j0 = blockIdx.y * JT;
-    const int b = bh / a.H, h = bh % a.H, dv = a.dv;
+    const int b = bh / a.H, h = bh % a.H, dv = a.dv, nc = a.n_chunks;
     const long long T = a.T, H = a.H, row0 = (long long)b * T * H + h;
     const int r = 16 * wave + lc;
-    const TIn *gq = (const TIn *)a.q, *gg = (const TIn *)a.g, *gt = (const TIn *)a.tau;
+    const TIn *gx = (const TIn *)(REV ? a.q : a.k), *gg = (const TIn *)a.g, *gt = (const TIn *)a.tau;
+    const TB *gb0 = REV ? (const TB *)a.dout : (const TB *)a.v, *gb1 = (const TB *)a.beta;
+    const float *x0 = REV ? a.dsf : a.s0;
+    float *xs = REV ? a.d_chunks : a.s_chunks;
+    float *xend = REV ? a.ds0 : a.s_final;
+    auto xoff = [&](int jt, int i) { return (size_t)(16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc; };
 
-    f32x4 D[NJ];
+    f32x4 X[NJ];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) D[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.dsf)
+    for (int jt = 0; jt < NJ; ++jt) X[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (x0)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                D[jt][i] = a.dsf[((size_t)bh * DK + 16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc];
+            for (int i = 0; i < 4; ++i) X[jt][i] = x0[(size_t)bh * DK * dv + xoff(jt, i)];
 
-    // next chunk's gates, kept raw (converted where used, so the loads stay in
-    // flight across the chunk in between)
-    typedef typename chunk_detail::InRaw<TIn>::type Raw;
-    Raw pq[NU][4], pg[NU][4], pt[NU][4];
-    f32x4 pd[LD];
-    auto prefetch = [&](int c) {
-        const long long c0 = (long long)c * C;
-        const long long lim = (T - c0) * H - h;                // token rows left from here
+    auto load = [&](int c, Regs &R) {
+        const long long c0 = (long long)c * C, lim = (T - c0) * H - h;
         const size_t bk = (size_t)(row0 + c0 * H) * DK, bv = (size_t)(row0 + c0 * H) * dv;
-        const rsrc_t Rq = make_rsrc(gq + bk, lim * DK * (long long)sizeof(TIn));
+        const rsrc_t Rx = make_rsrc(gx + bk, lim * DK * (long long)sizeof(TIn));
         const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * (long long)sizeof(TIn));
         const rsrc_t Rt = make_rsrc(gt + bk, lim * DK * (long long)sizeof(TIn));
-        const rsrc_t Rd = make_rsrc(a.dout + bv, lim * dv * 4);
 #pragma unroll
         for (int t = 0; t < NU; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const unsigned o = (unsigned)((16 * t + 4 * lg + i) * H * DK + r);
-                pq[t][i] = ld_raw<TIn>(Rq, o);
-                pg[t][i] = ld_raw<TIn>(Rg, o);
-                pt[t][i] = ld_raw<TIn>(Rt, o);
+                R.x[t][i] = ld_raw<TIn>(Rx, o);
+                R.g[t][i] = ld_raw<TIn>(Rg, o);
+                R.t[t][i] = ld_raw<TIn>(Rt, o);
             }
+        const rsrc_t Rb0 = make_rsrc(gb0 + bv, lim * dv * (long long)sizeof(TB));
+        const rsrc_t Rb1 = make_rsrc(gb1 + bv, REV ? 0 : lim * dv * (long long)sizeof(TB));
 #pragma unroll
-        for (int m = 0; m < LD; ++m) {
-            const int p = tid + m * NT, u = p / (JT / 4), j = (p % (JT / 4)) * 4;
-            const unsigned o = (unsigned)((u * H * dv + j0 + j) * 4);
-            pd[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(Rd, p < NPD ? o : 0x80000000u, 0, 0));
+        for (int m = 0; m < LB; ++m) {
+            const int p = tid + m * NT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
+            const unsigned o = p < NPB ? (unsigned)((u * H * dv + j0 + j) * (long long)sizeof(TB)) : 0x80000000u;
+            R.b0[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb0, o, 0, 0);
+            if constexpr (!REV) R.b1[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb1, o, 0, 0);
         }
     };
 
-    if (a.n_chunks > 0) prefetch(a.n_chunks - 1);
-    for (int c = a.n_chunks - 1; c >= 0; --c) {
-        // q e^{b} over the chunk (b from the chunk start, log2 units) and e^{b_L}
-        float qd[NU][4];
+    auto body = [&](int it, Regs &cur, Regs &nxt) {
+        const int c = REV ? nc - 1 - it : it;
+        // cumulative sum of g tau over the chunk (within the lane's 4 tokens,
+        // across the 4 lane groups, then across token tiles)
+        float cs[NU][4];
         float run = 0.f;
 #pragma unroll
         for (int t = 0; t < NU; ++t) {
-            float p[4], s = 0.f;
+            float s = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s = __builtin_fmaf(chunk_detail::in_to_f32(pg[t][i]), chunk_detail::in_to_f32(pt[t][i]), s);
-                p[i] = s;
+                s = __builtin_fmaf(chunk_detail::in_to_f32(cur.g[t][i]), chunk_detail::in_to_f32(cur.t[t][i]), s);
+                cs[t][i] = s;
             }
             float incl = s, y;
             y = __shfl_up(incl, 16); if (lg >= 1) incl += y;
             y = __shfl_up(incl, 32); if (lg >= 2) incl += y;
-            const float excl = incl - s, tot = __shfl(incl, 48 + lc);
+            const float base = run + incl - s, tot = __shfl(incl, 48 + lc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qd[t][i] = chunk_detail::in_to_f32(pq[t][i]) *
-                           __builtin_amdgcn_exp2f(-kLog2e * (run + excl + p[i]));
+            for (int i = 0; i < 4; ++i) cs[t][i] += base;
             run += tot;
         }
-        const float ebl = __builtin_amdgcn_exp2f(-kLog2e * run);
-        float *buf = sdo[c & 1];
+        float ad[NU][4];
 #pragma unroll
-        for (int m = 0; m < LD; ++m) {
-            const int p = tid + m * NT, u = p / (JT / 4), j = (p % (JT / 4)) * 4;
-            if (p < NPD) *(f32x4 *)(buf + u * PJ + j) = pd[m];
+        for (int t = 0; t < NU; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = chunk_detail::in_to_f32(cur.x[t][i]);
+                if constexpr (REV) {
+                    ad[t][i] = x * __builtin_amdgcn_exp2f(-kLog2e * cs[t][i]);                  // q e^{b}
+                } else {
+                    const float ah = gate_pow(chunk_detail::in_to_f32(cur.g[t][i]),
+                                              chunk_detail::in_to_f32(cur.t[t][i]));
+                    ad[t][i] = ah * x * __builtin_amdgcn_exp2f(-kLog2e * (run - cs[t][i]));      // k' e^{b_L - b}
+                }
+            }
+        const float ebl = __builtin_amdgcn_exp2f(-kLog2e * run);
+        // the staged operand of this chunk into LDS buffer it & 1
+        float *buf = smem + (it & 1) * C * PJ;
+#pragma unroll
+        for (int m = 0; m < LB; ++m) {
+            const int p = tid + m * NT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
+            if (p < NPB) {
+                if constexpr (REV) {
+                    *(f32x4 *)(buf + u * PJ + j) = __builtin_bit_cast(f32x4, cur.b0[m]);
+                } else {
+#pragma unroll
+                    for (int n4 = 0; n4 < EPB / 4; ++n4) {
+                        f32x4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int n = 4 * n4 + e;
+                            float vv, bb;
+                            if constexpr (EPB == 8) {
+                                vv = __uint_as_float((n & 1) ? (cur.b0[m][n >> 1] & 0xffff0000u) : (cur.b0[m][n >> 1] << 16));
+                                bb = __uint_as_float((n & 1) ? (cur.b1[m][n >> 1] & 0xffff0000u) : (cur.b1[m][n >> 1] << 16));
+                            } else {
+                                vv = __uint_as_float(cur.b0[m][n]);
+                                bb = __uint_as_float(cur.b1[m][n]);
+                            }
+                            o[e] = vv * bb;
+                        }
+                        *(f32x4 *)(buf + u * PJ + j + 4 * n4) = o;
+                    }
+                }
+            }
         }
-        if (c > 0) prefetch(c - 1);
+        if (it + 1 < nc) load(REV ? c - 1 : c + 1, nxt);
         __syncthreads();
-        float *wd = a.d_chunks + ((size_t)bh * a.n_chunks + c) * DK * dv;
+        float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_nontemporal_store(D[jt][i], wd + (size_t)(16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc);
+            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(X[jt][i], dst + xoff(jt, i));
         float el[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) el[i] = __shfl(ebl, 4 * lg + i);
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) D[jt][i] *= el[i];
+            for (int i = 0; i < 4; ++i) X[jt][i] *= el[i];
 #pragma unroll
         for (int ks = 0; ks < C / 32; ++ks) {
             float ax[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ax[e] = qd[2 * ks + (e >> 2)][e & 3];
+            for (int e = 0; e < 8; ++e) ax[e] = ad[2 * ks + (e >> 2)][e & 3];
             bf16x8 A[NS];
             split8<NS>(ax, A);
 #pragma unroll
@@ -246,16 +297,33 @@ __global__ __launch_bounds__(64 * (DK / 16)) void adjoint_sweep_kernel(SweepArgs
                 op_cols<C>(buf, PJ, 16 * jt + lc, 32 * ks, lg, bx);
                 bf16x8 Bv[NS];
                 split8<NS>(bx, Bv);
-                D[jt] = mma_split<NS>(A, Bv, D[jt]);
+                X[jt] = mma_split<NS>(A, Bv, X[jt]);
             }
         }
+    };
+
+    Regs R0, R1;
+    if (nc > 0) load(REV ? nc - 1 : 0, R0);
+    for (int it = 0; it < nc; it += 2) {
+        body(it, R0, R1);
+        if (it + 1 < nc) body(it + 1, R1, R0);
     }
-    if (a.ds0)
+    if (xend)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.ds0[((size_t)bh * DK + 16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc] = D[jt][i];
+            for (int i = 0; i < 4; ++i) xend[(size_t)bh * DK * dv + xoff(jt, i)] = X[jt][i];
+}
+
+// Both sweeps in one launch (blockIdx.z: 0 forward, 1 reverse); they are
+// independent and latency-bound, so their workgroups share the CUs.
+template <int DK, int JT, typename TIn>
+__global__ __launch_bounds__(64 * (DK / 16)) void state_sweeps_kernel(SweepArgs a)
+{
+    constexpr int C = ChunkOf<DK>::C, PJ = JT + 4;
+    __shared__ __attribute__((aligned(16))) float smem[2 * C * PJ];
+    if (blockIdx.z == 0) state_sweep<DK, JT, TIn, false>(a, smem);
+    else state_sweep<DK, JT, TIn, true>(a, smem);
 }
 
 // ------------------------------------------------------------------ (3) chunk gradients
@@ -265,29 +333,83 @@ struct GradArgs {
     const void *q, *k, *g, *tau, *v, *beta;
     const float *dout;
     const float *s_chunks;     // [B*H][n_chunks][DK][DV] S entering every chunk
-    const float *s_final;      // [B*H][DK][DV]
     const float *d_chunks;     // [B*H][n_chunks][DK][DV] D leaving every chunk
     float *dq, *dk, *dg, *dtau, *dv, *dbeta;
 };
 
-// LDS in floats, rows padded by 4 floats (16-byte aligned rows; the four k-slot
-// groups of a column-wise operand read land in distinct banks).
-template <int DK, int DV>
+typedef unsigned short u16;
+
+// The matrices the waves share go to LDS already split: NS planes of bf16
+// terms per matrix (plane n holds term n of every element), rows padded by 4
+// elements.  A row-wise MFMA operand is then two 8-byte reads per plane and no
+// arithmetic; a column-wise one is 8 two-byte reads per plane.
+template <int NS>
+__device__ __forceinline__ void split1(float x, u16 *t) {
+    unsigned w[NS];
+    chunk_detail::split_pair<NS>(x, 0.f, w);
+#pragma unroll
+    for (int n = 0; n < NS; ++n) t[n] = (u16)(w[n] & 0xffffu);
+}
+
+// x[e] = element (row, k0 + kslot(lg, e)) of a split matrix with planes pl
+// elements apart: operand A[n] for each term n
+template <int NS, int K>
+__device__ __forceinline__ void sop_rows(const u16 *p0, int pl, int pitch, int row, int k0, int lg, bf16x8 *A) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        const u16 *p = p0 + n * pl + row * pitch + k0 + 4 * lg;
+        const uint2 a = *(const uint2 *)p;
+        const uint2 b = K >= 32 ? *(const uint2 *)(p + 16) : uint2{0u, 0u};
+        A[n] = chunk_detail::pack8(a.x, a.y, b.x, b.y);
+    }
+}
+
+// x[e] = element (k0 + kslot(lg, e), col)
+template <int NS, int K>
+__device__ __forceinline__ void sop_cols(const u16 *p0, int pl, int pitch, int col, int k0, int lg, bf16x8 *A) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        unsigned w[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int e = 2 * e2;
+            const unsigned lo = (K >= 32 || e < 4) ? p0[n * pl + (k0 + kslot(lg, e)) * pitch + col] : 0u;
+            const unsigned hi = (K >= 32 || e < 4) ? p0[n * pl + (k0 + kslot(lg, e + 1)) * pitch + col] : 0u;
+            w[e2] = lo | (hi << 16);
+        }
+        A[n] = chunk_detail::pack8(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// LDS layout (bytes).  Split planes: Kt [C][DK]; Qt [C][DK], then A^T [C][C]
+// over it; one slab of JS dv columns of dO and V' [C][JS], then dA^T [C][C]
+// over dO.  The same area stages output rows as fp32: a slab of dv and
+// dbeta_hat [2][C][JS + 4] over the dO and V' planes, then dq, dk, dg, dtau
+// [4][C][DK + 4] over everything.
+template <int DK, int DV, int NS>
 struct GradCfg {
-    static constexpr int C = ChunkOf<DK>::C, NU = C / 16, NRB = DK / 16, NJT = DV / 16;
+    static constexpr int C = ChunkOf<DK>::C, NU = C / 16, NRB = DK / 16;
+    static constexpr int JS = DV < 64 ? DV : 64, NSL = DV / JS, NJS = JS / 16;   // dv slabs
     static constexpr int NW = NRB > 4 ? NRB : 4, NT = 64 * NW;
-    static constexpr int PK = DK + 4, PV = DV + 4, PC = C + 4;
-    static constexpr int o_qt = 0, o_kt = o_qt + C * PK, o_do = o_kt + C * PK, o_vp = o_do + C * PV;
-    static constexpr int end0 = o_vp + C * PV;
-    // A^T and dA^T are written once Qt and V' are no longer read: over them
-    // where the rows fit, else past the end
-    static constexpr int o_at = PC <= PK ? o_qt : end0;
-    static constexpr int end1 = PC <= PK ? end0 : end0 + C * PC;
-    static constexpr int o_dat = PC <= PV ? o_vp : end1;
-    static constexpr int end2 = PC <= PV ? end1 : end1 + C * PC;
-    static constexpr int o_f = end2;
-    static constexpr int floats = o_f + DK;
-    static constexpr size_t bytes = (size_t)floats * 4;
+    static constexpr int PK = DK + 4, PS = JS + 4, PC = C + 4;            // bf16 elements
+    static constexpr int LK = C * PK, LS = C * PS, LC = C * PC;           // plane sizes
+    static constexpr size_t o_kt = 0, o_qt = o_kt + (size_t)NS * LK * 2;
+    static constexpr size_t o_do = o_qt + (size_t)NS * LK * 2, o_vp = o_do + (size_t)NS * LS * 2;
+    static constexpr size_t end0 = o_vp + (size_t)NS * LS * 2;
+    static constexpr size_t o_at = PC <= PK ? o_qt : end0;
+    static constexpr size_t end1 = PC <= PK ? end0 : end0 + (size_t)NS * LC * 2;
+    static constexpr size_t o_dat = PC <= PS ? o_do : end1;
+    static constexpr size_t end2 = PC <= PS ? end1 : end1 + (size_t)NS * LC * 2;
+    static constexpr size_t o_f = end2;
+    static constexpr size_t end3 = o_f + (size_t)DK * 4;
+    static constexpr int OK = DK + 4, OS = JS + 4;                        // fp32 staging rows
+    static constexpr size_t stage_k = (size_t)4 * C * OK * 4;             // at 0
+    static constexpr size_t stage_v = (size_t)2 * C * OS * 4;             // at o_do
+    static constexpr size_t need_v = o_do + stage_v;
+    static constexpr size_t m01 = end3 > stage_k ? end3 : stage_k;
+    static constexpr size_t bytes = m01 > need_v ? m01 : need_v;
+    // the f vector must survive the dv staging
+    static_assert(o_f >= need_v || o_f + DK * 4 <= o_do, "f vs dv staging");
 };
 
 // One workgroup per (b, h, chunk).  Roles of wave w:
@@ -297,22 +419,32 @@ struct GradCfg {
 //     t = 2 ks, 2 ks + 1, the k-slots of step ks), then dQt and dKt of the block
 //     and the elementwise tail (dq, dk, dlambda, dg, dtau);
 //   token tile w (w < C/16): rows w of A^T and dA^T;
-//   dv tiles w, w + NW, ...: dV' of those 16 columns, then dv and dbeta_hat.
+//   dv tile w of each slab: dV' of those 16 columns, then dv and dbeta_hat.
+// The dv slabs are processed one after the other (dA^T, dQt and dKt
+// accumulate over them), which keeps the LDS small enough for two workgroups
+// per CU: one computes while the other waits for memory.
 template <int DK, int DV, typename TIn>
-__global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(GradArgs a)
+__global__ __launch_bounds__((GradCfg<DK, DV, 2>::NT), (DK <= 64 && !std::is_same<TIn, float>::value ? 2 : 1))
+void chunk_grad_kernel(GradArgs a)
 {
-    typedef GradCfg<DK, DV> L;
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    constexpr int C = L::C, NU = L::NU, NRB = L::NRB, NJT = L::NJT, NW = L::NW, NT = L::NT;
-    constexpr int PK = L::PK, PV = L::PV, PC = L::PC;
-    constexpr int KSC = C / 32, JPW = (NJT + NW - 1) / NW;
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *sQt = sm + L::o_qt, *sKt = sm + L::o_kt, *sdO = sm + L::o_do, *sVp = sm + L::o_vp;
-    float *sAt = sm + L::o_at, *sdAt = sm + L::o_dat, *sF = sm + L::o_f;
+    typedef GradCfg<DK, DV, NS> L;
+    constexpr int C = L::C, NU = L::NU, NRB = L::NRB, NW = L::NW, NT = L::NT;
+    constexpr int JS = L::JS, NSL = L::NSL, NJS = L::NJS;
+    constexpr int PK = L::PK, PS = L::PS, PC = L::PC, LK = L::LK, LS = L::LS, LC = L::LC;
+    constexpr int KSC = C / 32, KSK = (DK + 31) / 32, KSS = (JS + 31) / 32;
+    constexpr int OK = L::OK, OS = L::OS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    u16 *sKt = (u16 *)(smem + L::o_kt), *sQt = (u16 *)(smem + L::o_qt);
+    u16 *sdO = (u16 *)(smem + L::o_do), *sVp = (u16 *)(smem + L::o_vp);
+    u16 *sAt = (u16 *)(smem + L::o_at), *sdAt = (u16 *)(smem + L::o_dat);
+    float *sF = (float *)(smem + L::o_f);
+    float *sOutK = (float *)smem, *sOutV = (float *)(smem + L::o_do);
+    typedef typename chunk_detail::InRaw<TIn>::type Raw;
 
     // work item: workgroups are dealt to the 8 XCDs round-robin; give each XCD
-    // a contiguous range of (b, h, chunk), so the state a chunk reads as S_o is
-    // read as S_in by its neighbour on the same L2
+    // a contiguous range of (b, h, chunk), so neighbouring chunks of a head
+    // share an L2
     const int per_xcd = (a.n_work + 7) / 8;
     const int wi = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (wi >= a.n_work) return;
@@ -326,83 +458,30 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
     const TIn *gt = (const TIn *)a.tau, *gv = (const TIn *)a.v, *gb = (const TIn *)a.beta;
     constexpr size_t SD = (size_t)DK * DV;
     const float *Sin = a.s_chunks + ((size_t)bh * a.n_chunks + c) * SD;
-    const float *Sout = c + 1 < a.n_chunks ? Sin + SD : a.s_final + (size_t)bh * SD;
     const float *Dout = a.d_chunks + ((size_t)bh * a.n_chunks + c) * SD;
     // token rows of head h from the chunk start to the sequence end
     const long long lim = (T - c0) * H - h;
     const size_t bk = (size_t)(row0 + c0 * H) * DK, bv = (size_t)(row0 + c0 * H) * DV;
     constexpr long long ESZ = sizeof(TIn);
     const unsigned HK = (unsigned)(H * DK), HV = (unsigned)(H * DV);
-
-    // ---- dO and V' = beta_hat v of the chunk into LDS (16-byte pieces)
-    {
-        const rsrc_t Rd = make_rsrc(a.dout + bv, lim * DV * 4);
-        const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ);
-        const rsrc_t Rb = make_rsrc(gb + bv, lim * DV * ESZ);
-        constexpr int NPD = C * DV / 4, LPD = (NPD + NT - 1) / NT;
-        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-        constexpr int EPV = 16 / (int)sizeof(TIn);
-        constexpr int NPV = C * DV / EPV, LPV = (NPV + NT - 1) / NT;
-        u32x4v xd[LPD], xv[LPV], xb[LPV];
-#pragma unroll
-        for (int m = 0; m < LPD; ++m) {
-            const int p = tid + m * NT, u = p / (DV / 4), j = (p % (DV / 4)) * 4;
-            xd[m] = __builtin_amdgcn_raw_buffer_load_b128(Rd, p < NPD ? (u * HV + j) * 4u : 0x80000000u, 0, 0);
-        }
-#pragma unroll
-        for (int m = 0; m < LPV; ++m) {
-            const int p = tid + m * NT, u = p / (DV / EPV), j = (p % (DV / EPV)) * EPV;
-            const unsigned o = p < NPV ? (u * HV + j) * (unsigned)ESZ : 0x80000000u;
-            xv[m] = __builtin_amdgcn_raw_buffer_load_b128(Rv, o, 0, 0);
-            xb[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb, o, 0, 0);
-        }
-#pragma unroll
-        for (int m = 0; m < LPD; ++m) {
-            const int p = tid + m * NT, u = p / (DV / 4), j = (p % (DV / 4)) * 4;
-            if (p < NPD) *(f32x4 *)(sdO + u * PV + j) = __builtin_bit_cast(f32x4, xd[m]);
-        }
-#pragma unroll
-        for (int m = 0; m < LPV; ++m) {
-            const int p = tid + m * NT, u = p / (DV / EPV), j = (p % (DV / EPV)) * EPV;
-            if (p < NPV)
-#pragma unroll
-                for (int n4 = 0; n4 < EPV / 4; ++n4) {
-                    f32x4 o;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int n = 4 * n4 + e;
-                        float vv, bb;
-                        if constexpr (EPV == 8) {
-                            vv = __uint_as_float((n & 1) ? (xv[m][n >> 1] & 0xffff0000u) : (xv[m][n >> 1] << 16));
-                            bb = __uint_as_float((n & 1) ? (xb[m][n >> 1] & 0xffff0000u) : (xb[m][n >> 1] << 16));
-                        } else {
-                            vv = __uint_as_float(xv[m][n]);
-                            bb = __uint_as_float(xb[m][n]);
-                        }
-                        o[e] = vv * bb;
-                    }
-                    *(f32x4 *)(sVp + u * PV + j + 4 * n4) = o;
-                }
-        }
-    }
-
-    // ---- gates of this wave's dk block
     const bool rwave = wave < NRB;
     const int r = 16 * wave + lc;
-    float q_[NU][4], k_[NU][4], g_[NU][4], t_[NU][4], d_[NU][4], ah_[NU][4];
-    float ebm = 0.f, fl = 0.f;
+    const rsrc_t Rq = make_rsrc(gq + bk, lim * DK * ESZ), Rk = make_rsrc(gk + bk, lim * DK * ESZ);
+    const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * ESZ), Rt = make_rsrc(gt + bk, lim * DK * ESZ);
+    auto gate = [&](const rsrc_t &R, int t, int i) { return ld_tok<TIn>(R, (16 * t + 4 * lg + i) * HK + r); };
+
+    // ---- phase A: gates of this wave's dk block, Qt and Kt into LDS (split);
+    //      then A^T[s][u] = sum_r Kt[s][r] Qt[u][r] by token tiles, over Qt
+    float d_[NU][4];                       // b - b_m (log2 units) at (token, r)
+    float ebm = 0.f, fl = 0.f, ebl = 0.f;
     if (rwave) {
-        const rsrc_t Rq = make_rsrc(gq + bk, lim * DK * ESZ), Rk = make_rsrc(gk + bk, lim * DK * ESZ);
-        const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * ESZ), Rt = make_rsrc(gt + bk, lim * DK * ESZ);
+        float q_[NU][4], k_[NU][4], g_[NU][4], t_[NU][4];
 #pragma unroll
         for (int t = 0; t < NU; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const unsigned o = (16 * t + 4 * lg + i) * HK + r;
-                q_[t][i] = ld_tok<TIn>(Rq, o);
-                k_[t][i] = ld_tok<TIn>(Rk, o);
-                g_[t][i] = ld_tok<TIn>(Rg, o);
-                t_[t][i] = ld_tok<TIn>(Rt, o);
+                q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
+                g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
             }
         // b = inclusive cumulative sum of -g tau (log2 units): within the
         // lane's 4 tokens, across the 4 lane groups, then across token tiles
@@ -428,122 +507,289 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int u = 16 * t + 4 * lg + i;
-                d_[t][i] -= bm;                                    // b - b_m
-                ah_[t][i] = gate_pow(g_[t][i], t_[t][i]);
-                sQt[u * PK + r] = q_[t][i] * __builtin_amdgcn_exp2f(d_[t][i]);
-                sKt[u * PK + r] = ah_[t][i] * k_[t][i] * __builtin_amdgcn_exp2f(-d_[t][i]);
+                d_[t][i] -= bm;
+                u16 tq[NS], tk[NS];
+                split1<NS>(q_[t][i] * __builtin_amdgcn_exp2f(d_[t][i]), tq);
+                split1<NS>(gate_pow(g_[t][i], t_[t][i]) * k_[t][i] * __builtin_amdgcn_exp2f(-d_[t][i]), tk);
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    sQt[n * LK + u * PK + r] = tq[n];
+                    sKt[n * LK + u * PK + r] = tk[n];
+                }
             }
         ebm = __builtin_amdgcn_exp2f(bm);
         fl = __builtin_amdgcn_exp2f(bL - bm);
+        ebl = __builtin_amdgcn_exp2f(bL);
         if (lg == 0) sF[r] = fl;
     }
     __syncthreads();
-
-    // ---- score tiles: A^T[s][u] = sum_r Kt[s][r] Qt[u][r], dA^T[s][u] =
-    //      sum_j V'[s][j] dO[u][j], for the s tile of this wave and u tiles >= it
-    f32x4 at[NU], dat[NU];
-    if (wave < NU) {
+    {
+        f32x4 at[NU];
         const int st = wave;
+        if (st < NU) {
 #pragma unroll
-        for (int ut = 0; ut < NU; ++ut) { at[ut] = f32x4{0.f, 0.f, 0.f, 0.f}; dat[ut] = at[ut]; }
+            for (int ut = 0; ut < NU; ++ut) at[ut] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += 32) {
-            float x[8];
-            bf16x8 A[NS];
-            op_rows<DK>(sKt, PK, 16 * st + lc, k0, lg, x);
-            split8<NS>(x, A);
-#pragma unroll
-            for (int ut = 0; ut < NU; ++ut)
-                if (ut >= st) {
-                    bf16x8 Bv[NS];
-                    op_rows<DK>(sQt, PK, 16 * ut + lc, k0, lg, x);
-                    split8<NS>(x, Bv);
-                    at[ut] = mma_split<NS>(A, Bv, at[ut]);
-                }
-        }
-#pragma unroll
-        for (int k0 = 0; k0 < DV; k0 += 32) {
-            float x[8];
-            bf16x8 A[NS];
-            op_rows<DV>(sVp, PV, 16 * st + lc, k0, lg, x);
-            split8<NS>(x, A);
-#pragma unroll
-            for (int ut = 0; ut < NU; ++ut)
-                if (ut >= st) {
-                    bf16x8 Bv[NS];
-                    op_rows<DV>(sdO, PV, 16 * ut + lc, k0, lg, x);
-                    split8<NS>(x, Bv);
-                    dat[ut] = mma_split<NS>(A, Bv, dat[ut]);
-                }
-        }
-    }
-
-    // ---- state terms of dQt and dKt for this wave's dk block, and rowsum(S_o * D):
-    //      dQt += e^{b_m} dO S_in^T, dKt += f V' D^T (B operands straight from
-    //      the workspace rows r = 16 w + lc)
-    f32x4 dqt[NU], dkt[NU];
-    float rs = 0.f;
-    if (rwave) {
-#pragma unroll
-        for (int t = 0; t < NU; ++t) { dqt[t] = f32x4{0.f, 0.f, 0.f, 0.f}; dkt[t] = dqt[t]; }
-#pragma unroll
-        for (int k0 = 0; k0 < DV; k0 += 32) {
-            float s[8], d[8], so[8];
-            op_rows<DV>(Sin, DV, r, k0, lg, s);
-            op_rows<DV>(Dout, DV, r, k0, lg, d);
-            op_rows<DV>(Sout, DV, r, k0, lg, so);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                rs = __builtin_fmaf(so[e], d[e], rs);
-                s[e] *= ebm;
-                d[e] *= fl;
-            }
-            bf16x8 Bs[NS], Bd[NS];
-            split8<NS>(s, Bs);
-            split8<NS>(d, Bd);
-#pragma unroll
-            for (int t = 0; t < NU; ++t) {
-                float x[8];
+            for (int k0 = 0; k0 < DK; k0 += 32) {
                 bf16x8 A[NS];
-                op_rows<DV>(sdO, PV, 16 * t + lc, k0, lg, x);
-                split8<NS>(x, A);
-                dqt[t] = mma_split<NS>(A, Bs, dqt[t]);
-                op_rows<DV>(sVp, PV, 16 * t + lc, k0, lg, x);
-                split8<NS>(x, A);
-                dkt[t] = mma_split<NS>(A, Bd, dkt[t]);
+                sop_rows<NS, DK>(sKt, LK, PK, 16 * st + lc, k0, lg, A);
+#pragma unroll
+                for (int ut = 0; ut < NU; ++ut)
+                    if (ut >= st) {
+                        bf16x8 Bv[NS];
+                        sop_rows<NS, DK>(sQt, LK, PK, 16 * ut + lc, k0, lg, Bv);
+                        at[ut] = mma_split<NS>(A, Bv, at[ut]);
+                    }
             }
         }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
+        __syncthreads();                   // Qt no longer read
+        // A^T (causal: u >= s) over Qt; the tile left of an odd diagonal tile
+        // is read by the 32-deep steps and is zero
+        if (st < NU) {
+#pragma unroll
+            for (int ut = 0; ut < NU; ++ut)
+                if (ut >= st || ut + 1 == st)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s_ = 16 * st + 4 * lg + i, u = 16 * ut + lc;
+                        u16 ta[NS];
+                        split1<NS>(ut >= st && u >= s_ ? at[ut][i] : 0.f, ta);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) sAt[n * LC + s_ * PC + u] = ta[n];
+                    }
+        }
     }
-    __syncthreads();                       // Qt and V' no longer read
 
-    // ---- A^T and dA^T (causal: u >= s) into LDS; the tile left of an odd
-    //      diagonal tile is read by the 32-deep steps and is zero
+    // ---- phase B, one dv slab at a time: dA^T += V' dO^T (token tiles),
+    //      dQt += e^{b_m} dO S_in^T and dKt += f V' D^T (dk blocks), and the
+    //      slab's dV' = A^T dO + Kt diag(f) D, dv, dbeta_hat (dv tiles)
+    f32x4 dat[NU], dqt[NU], dkt[NU];
+    float sd = 0.f;                        // sum_j S_in[r][j] D[r][j]
+#pragma unroll
+    for (int t = 0; t < NU; ++t) {
+        dat[t] = f32x4{0.f, 0.f, 0.f, 0.f}; dqt[t] = dat[t]; dkt[t] = dat[t];
+    }
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+        const int j0 = sl * JS;
+        // dO and V' = beta_hat v of the slab into LDS, split (16-byte pieces)
+        {
+            const rsrc_t Rd = make_rsrc(a.dout + bv, lim * DV * 4);
+            const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ);
+            const rsrc_t Rb = make_rsrc(gb + bv, lim * DV * ESZ);
+            constexpr int NPD = C * JS / 4, LPD = (NPD + NT - 1) / NT;
+            typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+            constexpr int EPV = 16 / (int)sizeof(TIn);
+            constexpr int NPV = C * JS / EPV, LPV = (NPV + NT - 1) / NT;
+            u32x4v xd[LPD], xv[LPV], xb[LPV];
+#pragma unroll
+            for (int m = 0; m < LPD; ++m) {
+                const int p = tid + m * NT, u = p / (JS / 4), j = (p % (JS / 4)) * 4;
+                xd[m] = __builtin_amdgcn_raw_buffer_load_b128(Rd, p < NPD ? (u * HV + j0 + j) * 4u : 0x80000000u, 0, 0);
+            }
+#pragma unroll
+            for (int m = 0; m < LPV; ++m) {
+                const int p = tid + m * NT, u = p / (JS / EPV), j = (p % (JS / EPV)) * EPV;
+                const unsigned o = p < NPV ? (u * HV + j0 + j) * (unsigned)ESZ : 0x80000000u;
+                xv[m] = __builtin_amdgcn_raw_buffer_load_b128(Rv, o, 0, 0);
+                xb[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb, o, 0, 0);
+            }
+#pragma unroll
+            for (int m = 0; m < LPD; ++m) {
+                const int p = tid + m * NT, u = p / (JS / 4), j = (p % (JS / 4)) * 4;
+                if (p < NPD) {
+                    unsigned w0[NS], w1[NS];
+                    chunk_detail::split_pair<NS>(__uint_as_float(xd[m][0]), __uint_as_float(xd[m][1]), w0);
+                    chunk_detail::split_pair<NS>(__uint_as_float(xd[m][2]), __uint_as_float(xd[m][3]), w1);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) *(uint2 *)(sdO + n * LS + u * PS + j) = uint2{w0[n], w1[n]};
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < LPV; ++m) {
+                const int p = tid + m * NT, u = p / (JS / EPV), j = (p % (JS / EPV)) * EPV;
+                if (p < NPV) {
+                    unsigned w[EPV / 2][NS];
+#pragma unroll
+                    for (int q2 = 0; q2 < EPV / 2; ++q2) {
+                        float x0, x1;
+                        if constexpr (EPV == 8) {
+                            x0 = __uint_as_float(xv[m][q2] << 16) * __uint_as_float(xb[m][q2] << 16);
+                            x1 = __uint_as_float(xv[m][q2] & 0xffff0000u) * __uint_as_float(xb[m][q2] & 0xffff0000u);
+                        } else {
+                            x0 = __uint_as_float(xv[m][2 * q2]) * __uint_as_float(xb[m][2 * q2]);
+                            x1 = __uint_as_float(xv[m][2 * q2 + 1]) * __uint_as_float(xb[m][2 * q2 + 1]);
+                        }
+                        chunk_detail::split_pair<NS>(x0, x1, w[q2]);
+                    }
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        if constexpr (EPV == 8)
+                            *(uint4 *)(sVp + n * LS + u * PS + j) = uint4{w[0][n], w[1][n], w[2][n], w[3][n]};
+                        else
+                            *(uint2 *)(sVp + n * LS + u * PS + j) = uint2{w[0][n], w[1][n]};
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // dA^T[s][u] += sum_j V'[s][j] dO[u][j], s tile of this wave, u tiles >= it
+        if (wave < NU) {
+            const int st = wave;
+#pragma unroll
+            for (int k0 = 0; k0 < JS; k0 += 32) {
+                bf16x8 A[NS];
+                sop_rows<NS, JS>(sVp, LS, PS, 16 * st + lc, k0, lg, A);
+#pragma unroll
+                for (int ut = 0; ut < NU; ++ut)
+                    if (ut >= st) {
+                        bf16x8 Bv[NS];
+                        sop_rows<NS, JS>(sdO, LS, PS, 16 * ut + lc, k0, lg, Bv);
+                        dat[ut] = mma_split<NS>(A, Bv, dat[ut]);
+                    }
+            }
+        }
+        // state terms of the dk block (B operands: S_in and D rows r of the slab)
+        if (rwave) {
+#pragma unroll
+            for (int ks = 0; ks < KSS; ++ks) {
+                float s_[8], d[8];
+                op_rows<JS>(Sin, DV, r, j0 + 32 * ks, lg, s_);
+                op_rows<JS>(Dout, DV, r, j0 + 32 * ks, lg, d);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sd = __builtin_fmaf(s_[e], d[e], sd);
+                    s_[e] *= ebm;
+                    d[e] *= fl;
+                }
+                bf16x8 Bs[NS], Bd[NS];
+                split8<NS>(s_, Bs);
+                split8<NS>(d, Bd);
+#pragma unroll
+                for (int t = 0; t < NU; ++t) {
+                    bf16x8 A[NS];
+                    sop_rows<NS, JS>(sdO, LS, PS, 16 * t + lc, 32 * ks, lg, A);
+                    dqt[t] = mma_split<NS>(A, Bs, dqt[t]);
+                    sop_rows<NS, JS>(sVp, LS, PS, 16 * t + lc, 32 * ks, lg, A);
+                    dkt[t] = mma_split<NS>(A, Bd, dkt[t]);
+                }
+            }
+        }
+        // dV' of this wave's dv tile of the slab
+        f32x4 dvp[NU];
+        const int jt = wave;                           // tile within the slab
+        const int jg = j0 + 16 * jt + lc;              // this lane's dv column
+        Raw vr[NU][4], br[NU][4];
+        if (jt < NJS) {
+            const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ), Rb = make_rsrc(gb + bv, lim * DV * ESZ);
+#pragma unroll
+            for (int t = 0; t < NU; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned o = (16 * t + 4 * lg + i) * HV + jg;
+                    vr[t][i] = ld_raw<TIn>(Rv, o);
+                    br[t][i] = ld_raw<TIn>(Rb, o);
+                }
+#pragma unroll
+            for (int t = 0; t < NU; ++t) dvp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) {
+                bf16x8 Bv[NS];
+                sop_cols<NS, C>(sdO, LS, PS, 16 * jt + lc, 32 * ks, lg, Bv);
+#pragma unroll
+                for (int t = 0; t < NU; ++t)
+                    if (2 * ks + 1 >= t) {
+                        bf16x8 A[NS];
+                        sop_rows<NS, C>(sAt, LC, PC, 16 * t + lc, 32 * ks, lg, A);
+                        dvp[t] = mma_split<NS>(A, Bv, dvp[t]);
+                    }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) {
+                float y[8];
+                bf16x8 Bv[NS];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kk = 32 * ks + kslot(lg, e);
+                    y[e] = kk < DK ? Dout[(size_t)kk * DV + jg] * sF[kk] : 0.f;
+                }
+                split8<NS>(y, Bv);
+#pragma unroll
+                for (int t = 0; t < NU; ++t) {
+                    bf16x8 A[NS];
+                    sop_rows<NS, DK>(sKt, LK, PK, 16 * t + lc, 32 * ks, lg, A);
+                    dvp[t] = mma_split<NS>(A, Bv, dvp[t]);
+                }
+            }
+        }
+        __syncthreads();                   // the slab's dO and V' no longer read
+        if (jt < NJS)
+#pragma unroll
+            for (int t = 0; t < NU; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s_ = 16 * t + 4 * lg + i, j = 16 * jt + lc;
+                    sOutV[(0 * C + s_) * OS + j] = chunk_detail::in_to_f32(br[t][i]) * dvp[t][i];
+                    sOutV[(1 * C + s_) * OS + j] = chunk_detail::in_to_f32(vr[t][i]) * dvp[t][i];
+                }
+        __syncthreads();
+        {
+            constexpr int PR = JS / 4, NP = 2 * C * PR, LP = (NP + NT - 1) / NT;
+#pragma unroll
+            for (int m = 0; m < LP; ++m) {
+                const int p = tid + m * NT;
+                if (p < NP) {
+                    const int o = p / (C * PR), u = (p / PR) % C, j = (p % PR) * 4;
+                    const rsrc_t R = make_rsrc((o == 0 ? a.dv : a.dbeta) + bv, lim * DV * 4);   // wave-uniform
+                    const chunk_detail::u32x4 x = *(const chunk_detail::u32x4 *)(sOutV + (o * C + u) * OS + j);
+                    __builtin_amdgcn_raw_buffer_store_b128(x, R, (u * HV + j0 + j) * 4u, 0, 2);
+                }
+            }
+        }
+        __syncthreads();                   // staging read before the next slab's planes
+    }
+
+    // ---- phase C: dA^T into LDS (over dO), then dQt += dA Kt (s <= u) and
+    //      dKt += dA^T Qt (u >= s) with Kt and Qt of the dk block as B operands
+    //      (gates reloaded: they are L2-resident by now)
     if (wave < NU) {
         const int st = wave;
 #pragma unroll
         for (int ut = 0; ut < NU; ++ut)
-            if (ut >= st)
+            if (ut >= st || ut + 1 == st)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int s_ = 16 * st + 4 * lg + i, u = 16 * ut + lc;
-                    const bool keep = u >= s_;
-                    sAt[s_ * PC + u] = keep ? at[ut][i] : 0.f;
-                    sdAt[s_ * PC + u] = keep ? dat[ut][i] : 0.f;
+                    u16 td[NS];
+                    split1<NS>(ut >= st && u >= s_ ? dat[ut][i] : 0.f, td);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) sdAt[n * LC + s_ * PC + u] = td[n];
                 }
-        if (st & 1)
+    }
+    float q_[NU][4], k_[NU][4], g_[NU][4], t_[NU][4], ah_[NU][4];
+    float rs = 0.f;
+    if (rwave) {
+#pragma unroll
+        for (int t = 0; t < NU; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int s_ = 16 * st + 4 * lg + i, u = 16 * (st - 1) + lc;
-                sAt[s_ * PC + u] = 0.f;
-                sdAt[s_ * PC + u] = 0.f;
+                q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
+                g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
             }
+        // rowsum(S_o * D)_r = e^{b_L} sum_j S_in[r][j] D[r][j] + sum_s Kt[s][r] (f V' D^T)[s][r]
+        // (S_o = diag(e^{b_L}) S_in + diag(f) Kt^T V'; dKt holds only its state term here)
+        rs = ebl * sd;
+#pragma unroll
+        for (int t = 0; t < NU; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ah_[t][i] = gate_pow(g_[t][i], t_[t][i]);
+                rs = __builtin_fmaf(ah_[t][i] * k_[t][i] * __builtin_amdgcn_exp2f(-d_[t][i]), dkt[t][i], rs);
+            }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
     }
     __syncthreads();
-
-    // ---- dQt += dA Kt (s <= u), dKt += dA^T Qt (u >= s); Kt and Qt of the
-    //      block as B operands from the gate registers
     if (rwave) {
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
@@ -559,73 +805,23 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
             split8<NS>(qx, BQ);
 #pragma unroll
             for (int t = 0; t < NU; ++t) {
-                float x[8];
                 bf16x8 A[NS];
                 if (2 * ks <= t) {                         // dA[u][s] = dA^T[s][u], u in tile t
-                    op_cols<C>(sdAt, PC, 16 * t + lc, 32 * ks, lg, x);
-                    split8<NS>(x, A);
+                    sop_cols<NS, C>(sdAt, LC, PC, 16 * t + lc, 32 * ks, lg, A);
                     dqt[t] = mma_split<NS>(A, BK, dqt[t]);
                 }
                 if (2 * ks + 1 >= t) {                     // dA^T rows s in tile t
-                    op_rows<C>(sdAt, PC, 16 * t + lc, 32 * ks, lg, x);
-                    split8<NS>(x, A);
+                    sop_rows<NS, C>(sdAt, LC, PC, 16 * t + lc, 32 * ks, lg, A);
                     dkt[t] = mma_split<NS>(A, BQ, dkt[t]);
                 }
             }
         }
     }
-
-    // ---- dV' = A^T dO + Kt diag(f) D for this wave's dv tiles
-    f32x4 dvp[JPW][NU];
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-        const int jt = wave + jj * NW;
-        if (jt < NJT) {
-#pragma unroll
-            for (int t = 0; t < NU; ++t) dvp[jj][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) {
-                float y[8];
-                bf16x8 Bv[NS];
-                op_cols<C>(sdO, PV, 16 * jt + lc, 32 * ks, lg, y);
-                split8<NS>(y, Bv);
-#pragma unroll
-                for (int t = 0; t < NU; ++t)
-                    if (2 * ks + 1 >= t) {
-                        float x[8];
-                        bf16x8 A[NS];
-                        op_rows<C>(sAt, PC, 16 * t + lc, 32 * ks, lg, x);
-                        split8<NS>(x, A);
-                        dvp[jj][t] = mma_split<NS>(A, Bv, dvp[jj][t]);
-                    }
-            }
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32) {
-                float y[8];
-                bf16x8 Bv[NS];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kk = k0 + kslot(lg, e);
-                    y[e] = kk < DK ? Dout[(size_t)kk * DV + 16 * jt + lc] * sF[kk] : 0.f;
-                }
-                split8<NS>(y, Bv);
-#pragma unroll
-                for (int t = 0; t < NU; ++t) {
-                    float x[8];
-                    bf16x8 A[NS];
-                    op_rows<DK>(sKt, PK, 16 * t + lc, k0, lg, x);
-                    split8<NS>(x, A);
-                    dvp[jj][t] = mma_split<NS>(A, Bv, dvp[jj][t]);
-                }
-            }
-        }
-    }
+    __syncthreads();                       // the LDS now stages dq, dk, dg, dtau
 
     // ---- elementwise tail of the dk block: dq, dk, then dlambda as a suffix
     //      sum over the chunk's tokens (+ rowsum(S_o D)), dg and dtau
     if (rwave) {
-        const rsrc_t Rq = make_rsrc(a.dq + bk, lim * DK * 4), Rk = make_rsrc(a.dk + bk, lim * DK * 4);
-        const rsrc_t Rg = make_rsrc(a.dg + bk, lim * DK * 4), Rt = make_rsrc(a.dtau + bk, lim * DK * 4);
         float carry = rs;
 #pragma unroll
         for (int t = NU - 1; t >= 0; --t) {
@@ -637,8 +833,8 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
                 const float dkp = __builtin_amdgcn_exp2f(-d_[t][i]) * dkt[t][i];     // dL/dk'
                 x[i] = q_[t][i] * dqv - ah_[t][i] * k_[t][i] * dkp;
                 dah[i] = k_[t][i] * dkp;                                        // dL/d(g^tau)
-                st_tok(Rq, u * HK + r, dqv);
-                st_tok(Rk, u * HK + r, ah_[t][i] * dkp);
+                sOutK[(0 * C + u) * OK + r] = dqv;
+                sOutK[(1 * C + u) * OK + r] = ah_[t][i] * dkp;
             }
             float sfx[4];
             sfx[3] = x[3];
@@ -658,38 +854,25 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
                     dgv += tv * ah_[t][i] * __builtin_amdgcn_rcpf(gv_) * dah[i];
                     dtv += ah_[t][i] * (__builtin_amdgcn_logf(gv_) * (1.f / kLog2e)) * dah[i];
                 }
-                st_tok(Rg, u * HK + r, dgv);
-                st_tok(Rt, u * HK + r, dtv);
+                sOutK[(2 * C + u) * OK + r] = dgv;
+                sOutK[(3 * C + u) * OK + r] = dtv;
             }
             carry += tot;
         }
     }
-
-    // ---- dv = beta_hat dV', dbeta_hat = v dV'
+    __syncthreads();
+    // whole rows to HBM (16-byte non-temporal stores; rows past T dropped by the range)
     {
-        const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ), Rb = make_rsrc(gb + bv, lim * DV * ESZ);
-        const rsrc_t Rdv = make_rsrc(a.dv + bv, lim * DV * 4), Rdb = make_rsrc(a.dbeta + bv, lim * DV * 4);
+        constexpr int PR = DK / 4, NP = 4 * C * PR, LP = (NP + NT - 1) / NT;
 #pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) {
-            const int jt = wave + jj * NW;
-            if (jt < NJT) {
-                float vv[NU][4], bb[NU][4];
-#pragma unroll
-                for (int t = 0; t < NU; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const unsigned o = (16 * t + 4 * lg + i) * HV + 16 * jt + lc;
-                        vv[t][i] = ld_tok<TIn>(Rv, o);
-                        bb[t][i] = ld_tok<TIn>(Rb, o);
-                    }
-#pragma unroll
-                for (int t = 0; t < NU; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const unsigned o = (16 * t + 4 * lg + i) * HV + 16 * jt + lc;
-                        st_tok(Rdv, o, bb[t][i] * dvp[jj][t][i]);
-                        st_tok(Rdb, o, vv[t][i] * dvp[jj][t][i]);
-                    }
+        for (int m = 0; m < LP; ++m) {
+            const int p = tid + m * NT;
+            if (p < NP) {
+                const int o = p / (C * PR), u = (p / PR) % C, j = (p % PR) * 4;
+                float *d = o == 0 ? a.dq : o == 1 ? a.dk : o == 2 ? a.dg : a.dtau;    // wave-uniform
+                const rsrc_t R = make_rsrc(d + bk, lim * DK * 4);
+                const chunk_detail::u32x4 x = *(const chunk_detail::u32x4 *)(sOutK + (o * C + u) * OK + j);
+                __builtin_amdgcn_raw_buffer_store_b128(x, R, (u * HK + j) * 4u, 0, 2);
             }
         }
     }
@@ -698,15 +881,16 @@ __global__ __launch_bounds__((GradCfg<DK, DV>::NT), 1) void chunk_grad_kernel(Gr
 template <int DK, int DV, typename TIn>
 hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
 {
-    typedef GradCfg<DK, DV> L;
+    typedef GradCfg<DK, DV, std::is_same<TIn, float>::value ? 3 : 2> L;
     constexpr int C = L::C;
     const int n_chunks = (Lc.T + C - 1) / C, BH = Lc.B * Lc.H;
     constexpr int JT = DV < 64 ? DV : 64;
     SweepArgs sa;
     sa.T = Lc.T; sa.H = Lc.H; sa.dv = DV; sa.n_chunks = n_chunks;
-    sa.q = Lc.in.q; sa.g = Lc.in.g; sa.tau = Lc.in.tau;
-    sa.dout = Lc.dout; sa.dsf = Lc.dsf; sa.d_chunks = Lc.d_chunks; sa.ds0 = Lc.ds0;
-    hipLaunchKernelGGL((adjoint_sweep_kernel<DK, JT, TIn>), dim3(BH, DV / JT), dim3(64 * (DK / 16)), 0,
+    sa.q = Lc.in.q; sa.k = Lc.in.k; sa.g = Lc.in.g; sa.tau = Lc.in.tau; sa.v = Lc.in.v; sa.beta = Lc.in.beta;
+    sa.s0 = Lc.s0; sa.dout = Lc.dout; sa.dsf = Lc.dsf;
+    sa.s_chunks = Lc.s_chunks; sa.s_final = Lc.s_final; sa.d_chunks = Lc.d_chunks; sa.ds0 = Lc.ds0;
+    hipLaunchKernelGGL((state_sweeps_kernel<DK, JT, TIn>), dim3(BH, DV / JT, 2), dim3(64 * (DK / 16)), 0,
                        stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -722,7 +906,7 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     ga.T = Lc.T; ga.H = Lc.H; ga.n_chunks = n_chunks; ga.n_work = BH * n_chunks;
     ga.q = Lc.in.q; ga.k = Lc.in.k; ga.g = Lc.in.g; ga.tau = Lc.in.tau; ga.v = Lc.in.v;
     ga.beta = Lc.in.beta; ga.dout = Lc.dout;
-    ga.s_chunks = Lc.s_chunks; ga.s_final = Lc.s_final; ga.d_chunks = Lc.d_chunks;
+    ga.s_chunks = Lc.s_chunks; ga.d_chunks = Lc.d_chunks;
     ga.dq = Lc.dq; ga.dk = Lc.dk_; ga.dg = Lc.dg; ga.dtau = Lc.dtau; ga.dv = Lc.dv_; ga.dbeta = Lc.dbeta;
     const int grid = 8 * ((ga.n_work + 7) / 8);
     hipLaunchKernelGGL((chunk_grad_kernel<DK, DV, TIn>), dim3(grid), dim3(L::NT), L::bytes, stream, ga);
@@ -735,9 +919,11 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(32, 16) X(32, 32) X(32, 64) X(32, 128)    \
     X(64, 16) X(64, 32) X(64, 64) X(64, 128) X(128, 16) X(128, 32) X(128, 64) X(128, 128)
 
-size_t chunk_bwd_lds_bytes(int dk, int dv)
+size_t chunk_bwd_lds_bytes(int dk, int dv, bool f32_inputs)
 {
-#define RODIMUS_BWD_LDS(XK, XV) if (dk == XK && dv == XV) return bwd_detail::GradCfg<XK, XV>::bytes;
+#define RODIMUS_BWD_LDS(XK, XV)                                                                  \
+    if (dk == XK && dv == XV)                                                                     \
+        return f32_inputs ? bwd_detail::GradCfg<XK, XV, 3>::bytes : bwd_detail::GradCfg<XK, XV, 2>::bytes;
     RODIMUS_BWD_SHAPES(RODIMUS_BWD_LDS)
 #undef RODIMUS_BWD_LDS
     return 0;

@@ -55,21 +55,22 @@ hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStre
 hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
                          float *state, float *out, hipStream_t stream);
 
-// Backward of the chunk forward: given the forward's state entering every
-// chunk (a state-only forward sweep at the same chunk length), one adjoint
-// sweep writes dL/dS leaving every chunk and dL/dS_0, then one workgroup per
-// (b, h, chunk) forms the chunk's gradients.
+// Backward of the chunk forward: one launch runs the forward state sweep
+// (the state entering every chunk, and S_T) and the reverse adjoint sweep
+// (dL/dS leaving every chunk, and dL/dS_0) side by side; then one workgroup
+// per (b, h, chunk) forms the chunk's gradients.
 struct ChunkBwdLaunch {
     int B, T, H, dk, dv;
     bool f32_inputs;
     TokenInputs in;
+    const float *s0;        // [B*H][dk][dv] initial state or null
     const float *dout, *dsf;
-    const float *s_chunks;  // [B*H][ceil(T / chunk)][dk][dv] chunk-start states
-    const float *s_final;   // [B*H][dk][dv] final state
+    float *s_chunks;        // [B*H][ceil(T / chunk)][dk][dv] chunk-start states (written)
+    float *s_final;         // [B*H][dk][dv] final state (written)
     float *d_chunks;        // [B*H][ceil(T / chunk)][dk][dv] dL/dS leaving every chunk (written)
     float *dq, *dk_, *dg, *dtau, *dv_, *dbeta, *ds0;
 };
-size_t chunk_bwd_lds_bytes(int dk, int dv);   // 0 if the shape is not instantiated
+size_t chunk_bwd_lds_bytes(int dk, int dv, bool f32_inputs);   // 0 if the shape is not instantiated
 int chunk_bwd_chunk(int dk);                   // tokens per chunk of the backward
 hipError_t launch_chunk_bwd(const ChunkBwdLaunch &L, hipStream_t stream);
 
