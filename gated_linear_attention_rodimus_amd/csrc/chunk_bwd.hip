@@ -140,11 +140,17 @@ struct SweepArgs {
 // (V' or dO) is staged in LDS, two buffers.  The next chunk's inputs are loaded
 // into the other of two register sets (the loop is unrolled by two, so no
 // register copies wait on them) while the current chunk is processed.
+template <int DK> struct SweepWaves {
+    // at least 4 waves stage the operand; waves below DK/16 also own 16 state rows each
+    static constexpr int NRB = DK / 16, NW = NRB > 4 ? NRB : 4;
+};
+
 template <int DK, int JT, typename TIn, bool REV>
 __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    constexpr int C = ChunkOf<DK>::C, NU = C / 16, NW = DK / 16, NT = 64 * NW;
+    constexpr int C = ChunkOf<DK>::C, NU = C / 16, NRB = SweepWaves<DK>::NRB, NW = SweepWaves<DK>::NW;
+    constexpr int NT = 64 * NW;
     constexpr int NJ = JT / 16, PJ = JT + 4;
     typedef typename std::conditional<REV, float, TIn>::type TB;   // staged operand input type
     constexpr int EPB = 16 / (int)sizeof(TB), NPB = C * JT / EPB, LB = (NPB + NT - 1) / NT;
@@ -168,10 +174,11 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
     float *xend = REV ? a.ds0 : a.s_final;
     auto xoff = [&](int jt, int i) { return (size_t)(16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc; };
 
+    const bool rw = wave < NRB;            // owns state rows 16 wave .. 16 wave + 15
     f32x4 X[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) X[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (x0)
+    if (x0 && rw)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
@@ -183,15 +190,16 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
         const rsrc_t Rx = make_rsrc(gx + bk, lim * DK * (long long)sizeof(TIn));
         const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * (long long)sizeof(TIn));
         const rsrc_t Rt = make_rsrc(gt + bk, lim * DK * (long long)sizeof(TIn));
+        if (rw)
 #pragma unroll
-        for (int t = 0; t < NU; ++t)
+            for (int t = 0; t < NU; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const unsigned o = (unsigned)((16 * t + 4 * lg + i) * H * DK + r);
-                R.x[t][i] = ld_raw<TIn>(Rx, o);
-                R.g[t][i] = ld_raw<TIn>(Rg, o);
-                R.t[t][i] = ld_raw<TIn>(Rt, o);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned o = (unsigned)((16 * t + 4 * lg + i) * H * DK + r);
+                    R.x[t][i] = ld_raw<TIn>(Rx, o);
+                    R.g[t][i] = ld_raw<TIn>(Rg, o);
+                    R.t[t][i] = ld_raw<TIn>(Rt, o);
+                }
         const rsrc_t Rb0 = make_rsrc(gb0 + bv, lim * dv * (long long)sizeof(TB));
         const rsrc_t Rb1 = make_rsrc(gb1 + bv, REV ? 0 : lim * dv * (long long)sizeof(TB));
 #pragma unroll
@@ -205,6 +213,8 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
 
     auto body = [&](int it, Regs &cur, Regs &nxt) {
         const int c = REV ? nc - 1 - it : it;
+        float ad[NU][4], ebl = 0.f;
+        if (rw) {
         // cumulative sum of g tau over the chunk (within the lane's 4 tokens,
         // across the 4 lane groups, then across token tiles)
         float cs[NU][4];
@@ -225,7 +235,6 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
             for (int i = 0; i < 4; ++i) cs[t][i] += base;
             run += tot;
         }
-        float ad[NU][4];
 #pragma unroll
         for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -239,7 +248,8 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
                     ad[t][i] = ah * x * __builtin_amdgcn_exp2f(-kLog2e * (run - cs[t][i]));      // k' e^{b_L - b}
                 }
             }
-        const float ebl = __builtin_amdgcn_exp2f(-kLog2e * run);
+        ebl = __builtin_amdgcn_exp2f(-kLog2e * run);
+        }
         // the staged operand of this chunk into LDS buffer it & 1
         float *buf = smem + (it & 1) * C * PJ;
 #pragma unroll
@@ -272,6 +282,7 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
         }
         if (it + 1 < nc) load(REV ? c - 1 : c + 1, nxt);
         __syncthreads();
+        if (!rw) return;
         float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
@@ -308,7 +319,7 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
         body(it, R0, R1);
         if (it + 1 < nc) body(it + 1, R1, R0);
     }
-    if (xend)
+    if (xend && rw)
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
@@ -318,12 +329,11 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
 // Both sweeps in one launch (blockIdx.z: 0 forward, 1 reverse); they are
 // independent and latency-bound, so their workgroups share the CUs.
 template <int DK, int JT, typename TIn>
-__global__ __launch_bounds__(64 * (DK / 16)) void state_sweeps_kernel(SweepArgs a)
+__global__ __launch_bounds__((64 * SweepWaves<DK>::NW)) void state_sweeps_kernel(SweepArgs a)
 {
-    constexpr int C = ChunkOf<DK>::C, PJ = JT + 4;
-    __shared__ __attribute__((aligned(16))) float smem[2 * C * PJ];
-    if (blockIdx.z == 0) state_sweep<DK, JT, TIn, false>(a, smem);
-    else state_sweep<DK, JT, TIn, true>(a, smem);
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (blockIdx.z == 0) state_sweep<DK, JT, TIn, false>(a, (float *)smem);
+    else state_sweep<DK, JT, TIn, true>(a, (float *)smem);
 }
 
 // ------------------------------------------------------------------ (3) chunk gradients
@@ -884,14 +894,22 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     typedef GradCfg<DK, DV, std::is_same<TIn, float>::value ? 3 : 2> L;
     constexpr int C = L::C;
     const int n_chunks = (Lc.T + C - 1) / C, BH = Lc.B * Lc.H;
-    constexpr int JT = DV < 64 ? DV : 64;
+    constexpr int JT = DV;                 // one workgroup per (b, h) and direction
+    constexpr size_t sweep_lds = (size_t)2 * C * (JT + 4) * 4;
+    static bool sweep_attr_set = false;
+    if (!sweep_attr_set) {
+        hipError_t e0 = hipFuncSetAttribute((const void *)state_sweeps_kernel<DK, JT, TIn>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds);
+        if (e0 != hipSuccess) return e0;
+        sweep_attr_set = true;
+    }
     SweepArgs sa;
     sa.T = Lc.T; sa.H = Lc.H; sa.dv = DV; sa.n_chunks = n_chunks;
     sa.q = Lc.in.q; sa.k = Lc.in.k; sa.g = Lc.in.g; sa.tau = Lc.in.tau; sa.v = Lc.in.v; sa.beta = Lc.in.beta;
     sa.s0 = Lc.s0; sa.dout = Lc.dout; sa.dsf = Lc.dsf;
     sa.s_chunks = Lc.s_chunks; sa.s_final = Lc.s_final; sa.d_chunks = Lc.d_chunks; sa.ds0 = Lc.ds0;
-    hipLaunchKernelGGL((state_sweeps_kernel<DK, JT, TIn>), dim3(BH, DV / JT, 2), dim3(64 * (DK / 16)), 0,
-                       stream, sa);
+    hipLaunchKernelGGL((state_sweeps_kernel<DK, JT, TIn>), dim3(BH, DV / JT, 2), dim3(64 * SweepWaves<DK>::NW),
+                       sweep_lds, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
