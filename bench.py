@@ -228,7 +228,7 @@ def main():
         bus = e0.elapsed_time(e1) * 1e3 / args.bwd_steps
         ntok = B * T * H
         bbytes = ntok * ((4 * dk + 2 * dv) * 2 + 4 * dv + (4 * dk + 2 * dv) * 4)
-        backward = {"entry": "rodimus_ddts_chunk_bwd (state sweep + backward sweep)",
+        backward = {"entry": "rodimus_ddts_chunk_bwd (state sweeps + chunk gradients)",
                     "workload": args.workload, "calls": args.bwd_steps,
                     "us_per_call": round(bus, 1), "tokens_per_s": round(B * T / (bus * 1e-6), 1),
                     "algorithmic_bytes_per_call": bbytes,

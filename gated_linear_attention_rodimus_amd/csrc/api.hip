@@ -194,7 +194,6 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
     Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.gam_out = nullptr;
-    Lc.s_chunks = nullptr;
     const long long sz = (long long)dk * dv;
     if (P.segments == 1) {
         Lc.n_seg = 1; Lc.mode = 0;

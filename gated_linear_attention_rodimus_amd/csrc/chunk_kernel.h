@@ -240,7 +240,6 @@ struct Args {
     float *out;
     float *s_out; long long s_out_bh, s_out_seg; int s_out_last_only;
     float *gam_out;
-    float *s_chunks;             // [B*H][n_chunks][dk][dv]: state at every chunk start, or null
     int remap;                   // XCD-aware block mapping on/off
 };
 
@@ -640,13 +639,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
         const int cb = (it - 1) & 1;
 
         // ================= phase 1: S' and V' operands, state update
-        if (a.s_chunks && cwork) {           // the state entering chunk it - 1
-            float *sc = a.s_chunks + ((size_t)bh * a.n_chunks + (it - 1)) * DK * a.dv;
-#pragma unroll
-            for (int I = 0; I < NI; ++I)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[(size_t)(I * 16 + 4 * lg + r) * a.dv + jcol + lc] = S[I][r];
-        }
         bf16x8 sB[KSI][NS];
         if (cwork && outputs) {
             // B operands S' = diag(exp(b_m)) S_in (k = dk rows)
@@ -861,7 +853,6 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     a.s_out = Lc.s_out; a.s_out_bh = Lc.s_out_bh_stride; a.s_out_seg = Lc.s_out_seg_stride;
     a.s_out_last_only = Lc.s_out_last_only;
     a.gam_out = Lc.gam_out;
-    a.s_chunks = Lc.s_chunks;
     const long long blocks = (long long)Lc.B * Lc.H * Lc.n_seg * a.n_jt;
     a.remap = (blocks % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn, OUT>), dim3((unsigned)blocks), dim3(L::NT),

@@ -39,7 +39,6 @@ struct ChunkLaunch {
     float *out;
     float *s_out; long long s_out_bh_stride, s_out_seg_stride; int s_out_last_only;
     float *gam_out;         // [B*H][n_seg][dk] (mode 1)
-    float *s_chunks;        // [B*H][n_chunks][dk][dv] chunk-start states (one sweep), or null
 };
 hipError_t launch_chunk(const ChunkLaunch &L, hipStream_t stream);
 
