@@ -127,8 +127,10 @@ struct SweepArgs {
 };
 
 // The two sequential parts, one the mirror of the other, for one (b, h) and JT
-// columns of dv; wave w owns dk rows 16w..16w+15.  The state X lives in
-// registers in the MFMA C-layout (row 16 w + 4 lg + i, column 16 jt + lc).
+// columns of dv; wave w owns dk rows 16w..16w+15.  The state lives in
+// registers transposed, as MFMA C-layout tiles of X^T: lane (lc, lg) holds row
+// 16 w + lc at columns 16 jt + 4 lg .. + 3, so it scales its row by e^{b_L}
+// itself and stores the four values with one 16-byte store.
 //   forward (REV = false), chunks first to last:  store X = S entering the
 //     chunk, then S <- diag(e^{b_L}) S + (k' e^{b_L - b})^T V';
 //   reverse (REV = true), chunks last to first:  store X = D leaving the
@@ -136,7 +138,8 @@ struct SweepArgs {
 // with b the chunk's inclusive cumulative sum of -g tau, so both factors are
 // at most 1 in size.  The token-side factor is formed in the A-operand layout
 // directly: lane (lc, lg) holds column r = 16 w + lc at tokens 16 t + 4 lg + i,
-// which for t = 2 ks, 2 ks + 1 are the k-slots of step ks.  The other operand
+// which for t = 2 ks, 2 ks + 1 are the k-slots of step ks (the B operand of
+// X^T += B^T factor).  The other operand
 // (V' or dO) is staged in LDS, two buffers.  The next chunk's inputs are loaded
 // into the other of two register sets (the loop is unrolled by two, so no
 // register copies wait on them) while the current chunk is processed.
@@ -172,7 +175,8 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
     const float *x0 = REV ? a.dsf : a.s0;
     float *xs = REV ? a.d_chunks : a.s_chunks;
     float *xend = REV ? a.ds0 : a.s_final;
-    auto xoff = [&](int jt, int i) { return (size_t)(16 * wave + 4 * lg + i) * dv + j0 + 16 * jt + lc; };
+    // X^T tiles: lane (lc, lg) holds X[r][j0 + 16 jt + 4 lg .. + 3] for its row r = 16 wave + lc
+    auto xoff = [&](int jt) { return (size_t)r * dv + j0 + 16 * jt + 4 * lg; };
 
     const bool rw = wave < NRB;            // owns state rows 16 wave .. 16 wave + 15
     f32x4 X[NJ];
@@ -180,9 +184,7 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
     for (int jt = 0; jt < NJ; ++jt) X[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (x0 && rw)
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[jt][i] = x0[(size_t)bh * DK * dv + xoff(jt, i)];
+        for (int jt = 0; jt < NJ; ++jt) X[jt] = *(const f32x4 *)(x0 + (size_t)bh * DK * dv + xoff(jt));
 
     auto load = [&](int c, Regs &R) {
         const long long c0 = (long long)c * C, lim = (T - c0) * H - h;
@@ -285,16 +287,11 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
         if (!rw) return;
         float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(X[jt][i], dst + xoff(jt, i));
-        float el[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) el[i] = __shfl(ebl, 4 * lg + i);
+        for (int jt = 0; jt < NJ; ++jt) __builtin_nontemporal_store(X[jt], (f32x4 *)(dst + xoff(jt)));
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[jt][i] *= el[i];
+            for (int i = 0; i < 4; ++i) X[jt][i] *= ebl;                 // row r's decay
 #pragma unroll
         for (int ks = 0; ks < C / 32; ++ks) {
             float ax[8];
@@ -308,7 +305,7 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
                 op_cols<C>(buf, PJ, 16 * jt + lc, 32 * ks, lg, bx);
                 bf16x8 Bv[NS];
                 split8<NS>(bx, Bv);
-                X[jt] = mma_split<NS>(A, Bv, X[jt]);
+                X[jt] = mma_split<NS>(Bv, A, X[jt]);        // X^T += B^T (factor)
             }
         }
     };
@@ -321,9 +318,7 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
     }
     if (xend && rw)
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xend[(size_t)bh * DK * dv + xoff(jt, i)] = X[jt][i];
+        for (int jt = 0; jt < NJ; ++jt) *(f32x4 *)(xend + (size_t)bh * DK * dv + xoff(jt)) = X[jt];
 }
 
 // Both sweeps in one launch (blockIdx.z: 0 forward, 1 reverse); they are
