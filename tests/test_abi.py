@@ -108,9 +108,10 @@ def test_chunk_workspace_required_for_segments():
 
 
 def test_workspace_bytes_plan():
-    # one sweep when the heads fill the GPU: no workspace
+    # one sweep when the (b, h, dv tile) units fill more than half the CUs: no workspace
     assert R.workspace_bytes(8, 2048, 12, 64, 128) == 0
-    assert R.workspace_bytes(4, 4096, 16, 64, 128) == 0
+    # 64 heads x 2 dv tiles = half the CUs: two segments (transfers of both)
+    assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 2 * (64 * 128 + 64) * 4
     # long sequence, few heads: segmented
     ws = R.workspace_bytes(1, 65536, 16, 64, 128)
     assert ws > 0 and ws % (16 * (64 * 128 + 64) * 4) == 0
