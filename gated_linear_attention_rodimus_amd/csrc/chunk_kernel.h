@@ -457,6 +457,10 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     // it - 1.  The two roles run separate loops with the same barrier sequence,
     // so each is register-allocated on its own.
     if (producer) {
+        // the producers' operand preparation is the longer role of each chunk:
+        // let their instructions issue first on the SIMDs they share with
+        // consumers (measured ~2.5 % on the 130M layer)
+        __builtin_amdgcn_s_setprio(2);
         // raw inputs of two chunks (the current one and the next, in flight):
         // a dk column pair, TPG consecutive tokens
         Raw2 rq[2][TPG], rk[2][TPG], rg[2][TPG], rt[2][TPG];
