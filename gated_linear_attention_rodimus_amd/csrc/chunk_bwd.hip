@@ -66,9 +66,6 @@ template <typename TIn>
 __device__ __forceinline__ float ld_tok(rsrc_t r, unsigned off_elems) {
     return chunk_detail::in_to_f32(ld_raw<TIn>(r, off_elems));
 }
-__device__ __forceinline__ void st_tok(rsrc_t r, unsigned off_elems, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off_elems * 4u, 0, 2);   // non-temporal
-}
 
 // g^tau with pow semantics at g = 0
 __device__ __forceinline__ float gate_pow(float g, float tau) {
@@ -434,7 +431,7 @@ void chunk_grad_kernel(GradArgs a)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
     typedef GradCfg<DK, DV, NS> L;
-    constexpr int C = L::C, NU = L::NU, NRB = L::NRB, NW = L::NW, NT = L::NT;
+    constexpr int C = L::C, NU = L::NU, NRB = L::NRB, NT = L::NT;
     constexpr int JS = L::JS, NSL = L::NSL, NJS = L::NJS;
     constexpr int PK = L::PK, PS = L::PS, PC = L::PC, LK = L::LK, LS = L::LS, LC = L::LC;
     constexpr int KSC = C / 32, KSK = (DK + 31) / 32, KSS = (JS + 31) / 32;

@@ -335,9 +335,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     const int b = bh / a.H, h = bh % a.H;
     const int c_begin = seg * a.chunks_per_seg;
     const int c_end = min(a.n_chunks, c_begin + a.chunks_per_seg);
-    // pipeline steps: one per chunk plus one to drain, rounded up to even for
-    // the producers' two-step loop (the extra step only meets the barriers)
-    const int n_iter = (c_end - c_begin + 2) & ~1;
     constexpr bool outputs = OUT;           // mode 0: outputs; mode 1: segment transfer
 
     const int tid = threadIdx.x;
@@ -350,7 +347,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
     const int cp = tid % PP, cgp = tid / PP;           // producer: dk column pair owner
     const int c0 = 2 * cp;                             // its columns c0, c0 + 1
     const bool prep = producer && cgp < NG;
-    constexpr bool kAllPrep = NG * PP == 64 * NP;          // every producer lane has a group
 
     const long long T = a.T, H = a.H, dv = a.dv;
     const long long row_k = H * DK, row_v = H * dv;    // elements between tokens
@@ -749,7 +745,6 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
 
         // ================= phase 2: outputs
         if (cwork) {
-            const long long t0 = (long long)(it - 1) * C;
             if (outputs) {
                 // O = A V' + Qt S' for this wave's columns; the NU token tiles
                 // are independent accumulators, issued interleaved.
