@@ -212,6 +212,14 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
 
     auto body = [&](int it, Regs &cur, Regs &nxt) {
         const int c = REV ? nc - 1 - it : it;
+        // X (entering / leaving the chunk) to the workspace first: a wave has
+        // at most 63 memory operations in flight, and after the next chunk's
+        // loads are issued these stores would wait for them
+        if (rw) {
+            float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) __builtin_nontemporal_store(X[jt], (f32x4 *)(dst + xoff(jt)));
+        }
         float ad[NU][4], ebl = 0.f;
         if (rw) {
         // cumulative sum of g tau over the chunk (within the lane's 4 tokens,
@@ -282,9 +290,6 @@ __device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
         if (it + 1 < nc) load(REV ? c - 1 : c + 1, nxt);
         __syncthreads();
         if (!rw) return;
-        float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) __builtin_nontemporal_store(X[jt], (f32x4 *)(dst + xoff(jt)));
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
