@@ -25,17 +25,17 @@
 //
 // Only two things are sequential over chunks: the forward state S (entering
 // each chunk) and the state adjoint D (leaving each chunk).  So a call runs
-//   (1) the forward chunk kernel in state-only mode, which writes S_in of every
-//       chunk and S_T to the workspace;
-//   (2) adjoint_sweep_kernel: D backwards over the chunks by the dL/dS_in line
-//       above, one workgroup per (b, h, 64 dv columns), writing D of every
-//       chunk to the workspace and dL/dS_0;
+//   (1, 2) state_sweeps_kernel: S forwards and D backwards over the chunks
+//       (the S_o and dL/dS_in lines above), side by side in one launch, one
+//       workgroup per (b, h, dv tile) and direction, writing S_in and D of
+//       every chunk, S_T and dL/dS_0;
 //   (3) chunk_grad_kernel: one workgroup per (b, h, chunk), every chunk in
-//       parallel, forming all of the chunk's gradients from S_in, S_o and D.
+//       parallel, forming all of the chunk's gradients from S_in and D (the
+//       rowsum(S_o * D) term from S_in and the state term of dKt).
 // Every product is a 16x16-tile MFMA (v_mfma_f32_16x16x32_bf16, fp32
-// accumulate) whose fp32 operands are split into NS bf16 terms as they are
-// read (NS = 2 for bf16 inputs, 3 for fp32), as in the forward.  Tail tokens
-// read as zero (inert) and their gradients are not stored.
+// accumulate) whose fp32 operands are split into NS bf16 terms (NS = 2 for
+// bf16 inputs, 3 for fp32), as in the forward.  Tail tokens read as zero
+// (inert) and their gradients are not stored.
 #include "chunk_kernel.h"
 
 namespace rodimus {
@@ -102,14 +102,6 @@ __device__ __forceinline__ void op_rows(const float *p, int pitch, int row, int 
     }
 }
 
-// ... from an array whose columns run along k: x[e] = p[(k0 + kslot(lg, e)) * pitch + col].
-template <int K>
-__device__ __forceinline__ void op_cols(const float *p, int pitch, int col, int k0, int lg, float *x) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        x[e] = (K >= 32 || e < 4) ? p[(size_t)(k0 + kslot(lg, e)) * pitch + col] : 0.f;
-}
-
 // ------------------------------------------------------------------ (1, 2) state sweeps
 
 struct SweepArgs {
@@ -124,213 +116,327 @@ struct SweepArgs {
 };
 
 // The two sequential parts, one the mirror of the other, for one (b, h) and JT
-// columns of dv; wave w owns dk rows 16w..16w+15.  The state lives in
-// registers transposed, as MFMA C-layout tiles of X^T: lane (lc, lg) holds row
-// 16 w + lc at columns 16 jt + 4 lg .. + 3, so it scales its row by e^{b_L}
-// itself and stores the four values with one 16-byte store.
+// columns of dv:
 //   forward (REV = false), chunks first to last:  store X = S entering the
 //     chunk, then S <- diag(e^{b_L}) S + (k' e^{b_L - b})^T V';
 //   reverse (REV = true), chunks last to first:  store X = D leaving the
 //     chunk, then D <- diag(e^{b_L}) D + (q e^{b})^T dO;
 // with b the chunk's inclusive cumulative sum of -g tau, so both factors are
-// at most 1 in size.  The token-side factor is formed in the A-operand layout
-// directly: lane (lc, lg) holds column r = 16 w + lc at tokens 16 t + 4 lg + i,
-// which for t = 2 ks, 2 ks + 1 are the k-slots of step ks (the B operand of
-// X^T += B^T factor).  The other operand
-// (V' or dO) is staged in LDS, two buffers.  The next chunk's inputs are loaded
-// into the other of two register sets (the loop is unrolled by two, so no
-// register copies wait on them) while the current chunk is processed.
-template <int DK> struct SweepWaves {
-    // at least 4 waves stage the operand; waves below DK/16 also own 16 state rows each
-    static constexpr int NRB = DK / 16, NW = NRB > 4 ? NRB : 4;
+// at most 1 in size.  Two roles: NP producer waves turn a chunk into the
+// token-side factor and the staged operand (V' or dO), both split into NS
+// bf16 planes, token-major, in LDS buffer it & 1 of pipeline step it, while
+// the DK/16 state waves store X and add the product of the previous chunk
+// from the other buffer.  Two workgroup barriers per step:
+//   phase 1  producers: issue the next chunk's loads; cumulative sums of
+//            g tau over their tokens, scanned over the wave's token groups;
+//            the wave's per-column totals to LDS.
+//            state waves: X to the workspace (through LDS, whole rows).
+//   phase 2  producers: the other waves' totals complete the sums; factor
+//            planes, e^{b_L} per row, the staged operand planes.
+//            state waves: X decays by e^{b_L} and takes the MFMA product.
+// Memory access is by whole 128-byte lines where the layout allows: a
+// producer wave's lanes cover every dk column pair of GW tokens per load (one
+// 32-bit load per bf16 pair), the staged operand is read 16 bytes a lane along
+// rows, and each state wave's 16 rows of X (one contiguous block when JT = dv)
+// are written 16 bytes a lane after a pass through LDS.
+//   State waves: wave w owns dk rows 16 w .. 16 w + 15 of the state as MFMA
+// C-layout tiles of X^T (lane (lc, lg) holds row 16 w + lc at columns
+// 16 jt + 4 lg .. + 3, so the row decay is one scalar per lane).  Both MFMA
+// operands come from the planes through the transposing LDS read, which hands
+// lane (lc, lg) tokens 4 lg .. + 3 and 16 + 4 lg .. + 3 of a 32-token step,
+// the same k-slots for both.
+template <int DK, int JT, int NS_>
+struct SweepCfg {
+    static constexpr int NS = NS_;
+    static constexpr int C = ChunkOf<DK>::C;
+    // 4 producer waves; 8 for fp32 inputs at dk = 128, whose two register
+    // sets of pair loads would not fit beside 8 state waves
+    static constexpr int NP = DK == 128 && NS == 3 ? 8 : 4;
+    static constexpr int NRB = DK / 16, NW = NP + NRB, NT = 64 * NW;
+    static constexpr int PP = DK / 2;                          // dk column pairs
+    static constexpr int GW = 64 / PP;                         // token groups per producer wave
+    static constexpr int G = GW * NP, TPG = C / G;             // token groups, tokens per group
+    // plane row strides (bf16): four consecutive rows of a transposing read
+    // fall in distinct banks
+    static constexpr int RSA = DK == 16 ? 20 : DK == 32 ? 36 : DK == 64 ? 76 : 148;
+    static constexpr int RSB = JT + 16;
+    static constexpr int XS = JT + 4;                          // X staging row stride (fp32)
+    static constexpr size_t a_bytes = (size_t)NS * C * RSA * 2;     // factor planes
+    static constexpr size_t b_bytes = (size_t)NS * C * RSB * 2;     // staged operand planes
+    static constexpr size_t buf = a_bytes + b_bytes + (size_t)DK * 4;   // + e^{b_L} per row
+    static constexpr size_t t_off = 2 * buf;                   // [NP][DK] per-wave sums of g tau
+    static constexpr size_t x_off = t_off + (size_t)NP * DK * 4;    // [NRB][16][XS] X staging
+    static constexpr size_t bytes = x_off + (size_t)NRB * 16 * XS * 4;
+    static_assert(GW * PP == 64 && TPG * G == C && TPG >= 1, "producer lanes");
+    static_assert(C % 32 == 0 && JT % 16 == 0, "tile multiples");
 };
 
+// The dv tile of a sweep workgroup: the full dv, halved where the buffers
+// would not fit in LDS (fp32 inputs, dk = 64, dv = 128) or the registers of a
+// 16-wave workgroup (fp32 inputs, dk = dv = 128).
+template <int DK, int DV, int NS>
+struct SweepTile {
+    static constexpr bool halve = SweepCfg<DK, DV, NS>::bytes > 160 * 1024 || (NS == 3 && DK == 128 && DV == 128);
+    static constexpr int JT = halve ? DV / 2 : DV;
+};
+
+// acc[t] += the split product of A[t] and the shared operand Bv (term pairs
+// of total order < NS, smallest first) for NT independent tiles, issued
+// term-major so consecutive MFMAs never depend on each other.
+template <int NS, int NT>
+__device__ __forceinline__ void mma_split_shared(const bf16x8 (*A)[NS], const bf16x8 *Bv, f32x4 *acc) {
+    if constexpr (NS == 3) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][1], Bv[1], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[2], acc[t], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][2], Bv[0], acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[1], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][1], Bv[0], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t][0], Bv[0], acc[t], 0, 0, 0);
+}
+
 template <int DK, int JT, typename TIn, bool REV>
-__device__ __forceinline__ void state_sweep(const SweepArgs &a, float *smem)
+__device__ __forceinline__ void state_sweep(const SweepArgs &a, unsigned char *smem)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    constexpr int C = ChunkOf<DK>::C, NU = C / 16, NRB = SweepWaves<DK>::NRB, NW = SweepWaves<DK>::NW;
-    constexpr int NT = 64 * NW;
-    constexpr int NJ = JT / 16, PJ = JT + 4;
+    typedef SweepCfg<DK, JT, NS> L;
+    constexpr int C = L::C, NP = L::NP, NRB = L::NRB, PP = L::PP, GW = L::GW, TPG = L::TPG;
+    constexpr int RSA = L::RSA, RSB = L::RSB, XS = L::XS, NJ = JT / 16, KSC = C / 32, NPT = 64 * NP;
+    constexpr int JG = NJ < 4 ? NJ : NRB >= 8 ? 2 : 4;     // fewer operands live at 8 state waves
     typedef typename std::conditional<REV, float, TIn>::type TB;   // staged operand input type
-    constexpr int EPB = 16 / (int)sizeof(TB), NPB = C * JT / EPB, LB = (NPB + NT - 1) / NT;
-    typedef typename chunk_detail::InRaw<TIn>::type Raw;
+    constexpr int EPB = 16 / (int)sizeof(TB), NPB = C * JT / EPB, LB = (NPB + NPT - 1) / NPT;
+    typedef chunk_detail::Pair<TIn> PR;
+    typedef typename PR::type Raw2;
     typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-    struct Regs {
-        Raw x[NU][4], g[NU][4], t[NU][4];
-        u32x4v b0[LB], b1[REV ? 1 : LB];
-    };
 
-    const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x, j0 = blockIdx.y * JT;
     const int b = bh / a.H, h = bh % a.H, dv = a.dv, nc = a.n_chunks;
-    const long long T = a.T, H = a.H, row0 = (long long)b * T * H + h;
-    const int r = 16 * wave + lc;
-    const TIn *gx = (const TIn *)(REV ? a.q : a.k), *gg = (const TIn *)a.g, *gt = (const TIn *)a.tau;
-    const TB *gb0 = REV ? (const TB *)a.dout : (const TB *)a.v, *gb1 = (const TB *)a.beta;
-    const float *x0 = REV ? a.dsf : a.s0;
-    float *xs = REV ? a.d_chunks : a.s_chunks;
-    float *xend = REV ? a.ds0 : a.s_final;
-    // X^T tiles: lane (lc, lg) holds X[r][j0 + 16 jt + 4 lg .. + 3] for its row r = 16 wave + lc
-    auto xoff = [&](int jt) { return (size_t)r * dv + j0 + 16 * jt + 4 * lg; };
-
-    const bool rw = wave < NRB;            // owns state rows 16 wave .. 16 wave + 15
-    f32x4 X[NJ];
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) X[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (x0 && rw)
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) X[jt] = *(const f32x4 *)(x0 + (size_t)bh * DK * dv + xoff(jt));
-
-    auto load = [&](int c, Regs &R) {
-        const long long c0 = (long long)c * C, lim = (T - c0) * H - h;
-        const size_t bk = (size_t)(row0 + c0 * H) * DK, bv = (size_t)(row0 + c0 * H) * dv;
-        const rsrc_t Rx = make_rsrc(gx + bk, lim * DK * (long long)sizeof(TIn));
-        const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * (long long)sizeof(TIn));
-        const rsrc_t Rt = make_rsrc(gt + bk, lim * DK * (long long)sizeof(TIn));
-        if (rw)
-#pragma unroll
-            for (int t = 0; t < NU; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const unsigned o = (unsigned)((16 * t + 4 * lg + i) * H * DK + r);
-                    R.x[t][i] = ld_raw<TIn>(Rx, o);
-                    R.g[t][i] = ld_raw<TIn>(Rg, o);
-                    R.t[t][i] = ld_raw<TIn>(Rt, o);
-                }
-        const rsrc_t Rb0 = make_rsrc(gb0 + bv, lim * dv * (long long)sizeof(TB));
-        const rsrc_t Rb1 = make_rsrc(gb1 + bv, REV ? 0 : lim * dv * (long long)sizeof(TB));
-#pragma unroll
-        for (int m = 0; m < LB; ++m) {
-            const int p = tid + m * NT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
-            const unsigned o = p < NPB ? (unsigned)((u * H * dv + j0 + j) * (long long)sizeof(TB)) : 0x80000000u;
-            R.b0[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb0, o, 0, 0);
-            if constexpr (!REV) R.b1[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb1, o, 0, 0);
-        }
+    auto planeA = [&](int buf, int n) { return (__bf16 *)(smem + buf * L::buf) + (size_t)n * C * RSA; };
+    auto planeB = [&](int buf, int n) {
+        return (__bf16 *)(smem + buf * L::buf + L::a_bytes) + (size_t)n * C * RSB;
     };
+    auto ebl_of = [&](int buf) { return (float *)(smem + buf * L::buf + L::a_bytes + L::b_bytes); };
+    float *tots = (float *)(smem + L::t_off);
+    auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
 
-    auto body = [&](int it, Regs &cur, Regs &nxt) {
-        const int c = REV ? nc - 1 - it : it;
-        // X (entering / leaving the chunk) to the workspace first: a wave has
-        // at most 63 memory operations in flight, and after the next chunk's
-        // loads are issued these stores would wait for them
-        if (rw) {
-            float *dst = xs + ((size_t)bh * nc + c) * DK * dv;
+    if (wave >= NRB) {
+        // ------------------------------------------------ producers
+        const long long T = a.T, H = a.H, row0 = (long long)b * T * H + h;
+        const int ptid = tid - 64 * NRB, pw = wave - NRB, gw = lane / PP, pl = lane % PP;
+        const int gi = pw * GW + gw, c0 = 2 * pl;       // token group; dk columns c0, c0 + 1
+        const TIn *gx = (const TIn *)(REV ? a.q : a.k), *gg = (const TIn *)a.g, *gt = (const TIn *)a.tau;
+        const TB *gb0 = REV ? (const TB *)a.dout : (const TB *)a.v, *gb1 = (const TB *)a.beta;
+        struct Regs {
+            Raw2 x[TPG], g[TPG], t[TPG];
+            u32x4v b0[LB], b1[REV ? 1 : LB];
+        };
+        auto load = [&](int c, Regs &R) {
+            const long long t0 = (long long)c * C, lim = (T - t0) * H - h;
+            const size_t bk = (size_t)(row0 + t0 * H) * DK, bv = (size_t)(row0 + t0 * H) * dv;
+            const rsrc_t Rx = make_rsrc(gx + bk, lim * DK * (long long)sizeof(TIn));
+            const rsrc_t Rg = make_rsrc(gg + bk, lim * DK * (long long)sizeof(TIn));
+            const rsrc_t Rt = make_rsrc(gt + bk, lim * DK * (long long)sizeof(TIn));
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) __builtin_nontemporal_store(X[jt], (f32x4 *)(dst + xoff(jt)));
-        }
-        float ad[NU][4], ebl = 0.f;
-        if (rw) {
-        // cumulative sum of g tau over the chunk (within the lane's 4 tokens,
-        // across the 4 lane groups, then across token tiles)
-        float cs[NU][4];
-        float run = 0.f;
-#pragma unroll
-        for (int t = 0; t < NU; ++t) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s = __builtin_fmaf(chunk_detail::in_to_f32(cur.g[t][i]), chunk_detail::in_to_f32(cur.t[t][i]), s);
-                cs[t][i] = s;
+            for (int m = 0; m < TPG; ++m) {
+                const unsigned o = (unsigned)(((gi * TPG + m) * H * DK + c0) * (long long)sizeof(TIn));
+                R.g[m] = PR::load(Rg, o);
+                R.t[m] = PR::load(Rt, o);
+                R.x[m] = PR::load(Rx, o);
             }
-            float incl = s, y;
-            y = __shfl_up(incl, 16); if (lg >= 1) incl += y;
-            y = __shfl_up(incl, 32); if (lg >= 2) incl += y;
-            const float base = run + incl - s, tot = __shfl(incl, 48 + lc);
+            const rsrc_t Rb0 = make_rsrc(gb0 + bv, lim * dv * (long long)sizeof(TB));
+            const rsrc_t Rb1 = make_rsrc(gb1 + bv, REV ? 0 : lim * dv * (long long)sizeof(TB));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cs[t][i] += base;
-            run += tot;
-        }
+            for (int m = 0; m < LB; ++m) {
+                const int p = ptid + m * NPT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
+                const unsigned o = p < NPB ? (unsigned)((u * H * dv + j0 + j) * (long long)sizeof(TB)) : 0x80000000u;
+                R.b0[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb0, o, 0, 0);
+                if constexpr (!REV) R.b1[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb1, o, 0, 0);
+            }
+        };
+        auto step = [&](int it, const Regs &R, Regs &nxt) {
+            const bool work = it < nc;
+            const int pb = it & 1;
+            // ---- phase 1: sums of g tau over the thread's tokens, scanned over
+            // the wave's GW token groups (lanes pl + PP gw); the wave totals to LDS
+            float cum0[TPG], cum1[TPG], ex0 = 0.f, ex1 = 0.f;
+            if (work) {
+                if (it + 1 < nc) load(chunk_of(it + 1), nxt);
+                float run0 = 0.f, run1 = 0.f;
 #pragma unroll
-        for (int t = 0; t < NU; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = chunk_detail::in_to_f32(cur.x[t][i]);
-                if constexpr (REV) {
-                    ad[t][i] = x * __builtin_amdgcn_exp2f(-kLog2e * cs[t][i]);                  // q e^{b}
-                } else {
-                    const float ah = gate_pow(chunk_detail::in_to_f32(cur.g[t][i]),
-                                              chunk_detail::in_to_f32(cur.t[t][i]));
-                    ad[t][i] = ah * x * __builtin_amdgcn_exp2f(-kLog2e * (run - cs[t][i]));      // k' e^{b_L - b}
+                for (int m = 0; m < TPG; ++m) {
+                    run0 = PR::gt_lo(R.g[m], R.t[m], run0);
+                    run1 = PR::gt_hi(R.g[m], R.t[m], run1);
+                    cum0[m] = run0;
+                    cum1[m] = run1;
                 }
+                float in0 = run0, in1 = run1;
+#pragma unroll
+                for (int s = 1; s < GW; s <<= 1) {
+                    const float y0 = __shfl_up(in0, s * PP), y1 = __shfl_up(in1, s * PP);
+                    if (gw >= s) { in0 += y0; in1 += y1; }
+                }
+                ex0 = in0 - run0;
+                ex1 = in1 - run1;
+                if (gw == GW - 1) *(float2 *)(tots + pw * DK + c0) = make_float2(in0, in1);
             }
-        ebl = __builtin_amdgcn_exp2f(-kLog2e * run);
-        }
-        // the staged operand of this chunk into LDS buffer it & 1
-        float *buf = smem + (it & 1) * C * PJ;
+            __syncthreads();
+            // ---- phase 2: the earlier waves' totals complete the sums; planes
+            if (work) {
+                float tot0 = 0.f, tot1 = 0.f;
 #pragma unroll
-        for (int m = 0; m < LB; ++m) {
-            const int p = tid + m * NT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
-            if (p < NPB) {
-                if constexpr (REV) {
-                    *(f32x4 *)(buf + u * PJ + j) = __builtin_bit_cast(f32x4, cur.b0[m]);
-                } else {
+                for (int w = 0; w < NP; ++w) {
+                    const float2 x = *(const float2 *)(tots + w * DK + c0);
+                    if (w < pw) { ex0 += x.x; ex1 += x.y; }
+                    tot0 += x.x;
+                    tot1 += x.y;
+                }
 #pragma unroll
-                    for (int n4 = 0; n4 < EPB / 4; ++n4) {
-                        f32x4 o;
+                for (int m = 0; m < TPG; ++m) {
+                    const float s0 = ex0 + cum0[m], s1 = ex1 + cum1[m];      // -b_u (nats)
+                    float f0, f1;
+                    if constexpr (REV) {                                          // q e^{b}
+                        f0 = PR::lo(R.x[m]) * __builtin_amdgcn_exp2f(-kLog2e * s0);
+                        f1 = PR::hi(R.x[m]) * __builtin_amdgcn_exp2f(-kLog2e * s1);
+                    } else {                                                      // k' e^{b_L - b}
+                        const float la0 = chunk_detail::log2_gate_pow(PR::lo(R.g[m]), PR::lo(R.t[m]));
+                        const float la1 = chunk_detail::log2_gate_pow(PR::hi(R.g[m]), PR::hi(R.t[m]));
+                        f0 = PR::lo(R.x[m]) * __builtin_amdgcn_exp2f(__builtin_fmaf(-kLog2e, tot0 - s0, la0));
+                        f1 = PR::hi(R.x[m]) * __builtin_amdgcn_exp2f(__builtin_fmaf(-kLog2e, tot1 - s1, la1));
+                    }
+                    unsigned w[NS];
+                    chunk_detail::split_pair<NS>(f0, f1, w);
+                    const int u = gi * TPG + m;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int n = 4 * n4 + e;
-                            float vv, bb;
-                            if constexpr (EPB == 8) {
-                                vv = __uint_as_float((n & 1) ? (cur.b0[m][n >> 1] & 0xffff0000u) : (cur.b0[m][n >> 1] << 16));
-                                bb = __uint_as_float((n & 1) ? (cur.b1[m][n >> 1] & 0xffff0000u) : (cur.b1[m][n >> 1] << 16));
+                    for (int n = 0; n < NS; ++n) *(unsigned *)(planeA(pb, n) + u * RSA + c0) = w[n];
+                }
+                if (gi == 0)
+                    *(float2 *)(ebl_of(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(-kLog2e * tot0),
+                                                               __builtin_amdgcn_exp2f(-kLog2e * tot1));
+                // the staged operand: V' = beta_hat v (forward) or dO (reverse)
+#pragma unroll
+                for (int m = 0; m < LB; ++m) {
+                    const int p = ptid + m * NPT, u = p / (JT / EPB), j = (p % (JT / EPB)) * EPB;
+                    if (p < NPB) {
+                        unsigned w[EPB / 2][NS];
+#pragma unroll
+                        for (int e = 0; e < EPB / 2; ++e) {
+                            float x0, x1;
+                            if constexpr (REV) {
+                                x0 = __uint_as_float(R.b0[m][2 * e]);
+                                x1 = __uint_as_float(R.b0[m][2 * e + 1]);
+                            } else if constexpr (EPB == 8) {
+                                x0 = __uint_as_float(R.b0[m][e] << 16) * __uint_as_float(R.b1[m][e] << 16);
+                                x1 = __uint_as_float(R.b0[m][e] & 0xffff0000u) *
+                                     __uint_as_float(R.b1[m][e] & 0xffff0000u);
                             } else {
-                                vv = __uint_as_float(cur.b0[m][n]);
-                                bb = __uint_as_float(cur.b1[m][n]);
+                                x0 = __uint_as_float(R.b0[m][2 * e]) * __uint_as_float(R.b1[m][2 * e]);
+                                x1 = __uint_as_float(R.b0[m][2 * e + 1]) * __uint_as_float(R.b1[m][2 * e + 1]);
                             }
-                            o[e] = vv * bb;
+                            chunk_detail::split_pair<NS>(x0, x1, w[e]);
                         }
-                        *(f32x4 *)(buf + u * PJ + j + 4 * n4) = o;
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            __bf16 *dst = planeB(pb, n) + u * RSB + j;
+                            if constexpr (EPB == 8) *(u32x4v *)dst = u32x4v{w[0][n], w[1][n], w[2][n], w[3][n]};
+                            else *(uint2 *)dst = make_uint2(w[0][n], w[1][n]);
+                        }
                     }
                 }
             }
+            __syncthreads();
+        };
+        Regs R0, R1;
+        if (nc > 0) load(chunk_of(0), R0);
+        for (int it = 0; it <= nc; it += 2) {
+            step(it, R0, R1);
+            if (it + 1 <= nc) step(it + 1, R1, R0);
         }
-        if (it + 1 < nc) load(REV ? c - 1 : c + 1, nxt);
-        __syncthreads();
-        if (!rw) return;
+    } else {
+        // ------------------------------------------------ state waves
+        const int lc = lane & 15, lg = lane >> 4, r = 16 * wave + lc;
+        const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
+        const float *x0 = REV ? a.dsf : a.s0;
+        float *xs = REV ? a.d_chunks : a.s_chunks;
+        float *xend = REV ? a.ds0 : a.s_final;
+        float *xst = (float *)(smem + L::x_off) + wave * 16 * XS;    // this wave's staging rows
+        auto xoff = [&](int jt) { return (size_t)r * dv + j0 + 16 * jt + 4 * lg; };
+        f32x4 X[NJ];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+        for (int jt = 0; jt < NJ; ++jt) X[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (x0)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[jt][i] *= ebl;                 // row r's decay
+            for (int jt = 0; jt < NJ; ++jt) X[jt] = *(const f32x4 *)(x0 + (size_t)bh * DK * dv + xoff(jt));
+        for (int it = 0; it <= nc; ++it) {
+            const int cb = (it - 1) & 1;
+            if (it >= 1) {
+                // X -> LDS -> rows 16 w .. 16 w + 15 of the chunk's slot, 16 bytes a lane
+                float *dst = xs + ((size_t)bh * nc + chunk_of(it - 1)) * DK * dv + (size_t)16 * wave * dv + j0;
 #pragma unroll
-        for (int ks = 0; ks < C / 32; ++ks) {
-            float ax[8];
+                for (int jt = 0; jt < NJ; ++jt) *(f32x4 *)(xst + lc * XS + 16 * jt + 4 * lg) = X[jt];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ax[e] = ad[2 * ks + (e >> 2)][e & 3];
-            bf16x8 A[NS];
-            split8<NS>(ax, A);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
-                float bx[8];
-                op_cols<C>(buf, PJ, 16 * jt + lc, 32 * ks, lg, bx);
-                bf16x8 Bv[NS];
-                split8<NS>(bx, Bv);
-                X[jt] = mma_split<NS>(Bv, A, X[jt]);        // X^T += B^T (factor)
+                for (int i = 0; i < NJ; ++i) {
+                    const int e = i * 256 + 4 * lane, row = e / JT, col = e % JT;
+                    __builtin_nontemporal_store(*(const f32x4 *)(xst + row * XS + col),
+                                                (f32x4 *)(dst + (size_t)row * dv + col));
+                }
             }
-        }
-    };
-
-    Regs R0, R1;
-    if (nc > 0) load(REV ? nc - 1 : 0, R0);
-    for (int it = 0; it < nc; it += 2) {
-        body(it, R0, R1);
-        if (it + 1 < nc) body(it + 1, R1, R0);
-    }
-    if (xend && rw)
+            __syncthreads();
+            if (it >= 1) {
+                const float ebl = ebl_of(cb)[r];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) *(f32x4 *)(xend + (size_t)bh * DK * dv + xoff(jt)) = X[jt];
+                for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) X[jt][i] *= ebl;            // row r's decay
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks) {
+                    bf16x8 Fa[NS];
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        const __bf16 *pa = planeA(cb, n) + (32 * ks + trow) * RSA + 16 * wave + tcol;
+                        Fa[n] = chunk_detail::cat(chunk_detail::lds_read_tr(pa),
+                                                  chunk_detail::lds_read_tr(pa + 16 * RSA));
+                    }
+                    // JG independent tiles at a time (term-major MFMA issue)
+#pragma unroll
+                    for (int jg = 0; jg < NJ; jg += JG) {
+                        bf16x8 Bt[JG][NS];
+#pragma unroll
+                        for (int q = 0; q < JG; ++q)
+#pragma unroll
+                            for (int n = 0; n < NS; ++n) {
+                                const __bf16 *pb = planeB(cb, n) + (32 * ks + trow) * RSB + 16 * (jg + q) + tcol;
+                                Bt[q][n] = chunk_detail::cat(chunk_detail::lds_read_tr(pb),
+                                                             chunk_detail::lds_read_tr(pb + 16 * RSB));
+                            }
+                        mma_split_shared<NS, JG>(Bt, Fa, X + jg);           // X^T += B^T factor
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        if (xend)
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) *(f32x4 *)(xend + (size_t)bh * DK * dv + xoff(jt)) = X[jt];
+    }
 }
 
 // Both sweeps in one launch (blockIdx.z: 0 forward, 1 reverse); they are
 // independent and latency-bound, so their workgroups share the CUs.
 template <int DK, int JT, typename TIn>
-__global__ __launch_bounds__((64 * SweepWaves<DK>::NW)) void state_sweeps_kernel(SweepArgs a)
+__global__ __launch_bounds__((SweepCfg<DK, JT, std::is_same<TIn, float>::value ? 3 : 2>::NT))
+void state_sweeps_kernel(SweepArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    if (blockIdx.z == 0) state_sweep<DK, JT, TIn, false>(a, (float *)smem);
-    else state_sweep<DK, JT, TIn, true>(a, (float *)smem);
+    if (blockIdx.z == 0) state_sweep<DK, JT, TIn, false>(a, smem);
+    else state_sweep<DK, JT, TIn, true>(a, smem);
 }
 
 // ------------------------------------------------------------------ (3) chunk gradients
@@ -891,8 +997,10 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     typedef GradCfg<DK, DV, std::is_same<TIn, float>::value ? 3 : 2> L;
     constexpr int C = L::C;
     const int n_chunks = (Lc.T + C - 1) / C, BH = Lc.B * Lc.H;
-    constexpr int JT = DV;                 // one workgroup per (b, h) and direction
-    constexpr size_t sweep_lds = (size_t)2 * C * (JT + 4) * 4;
+    constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
+    constexpr int JT = SweepTile<DK, DV, NS>::JT;     // one workgroup per (b, h, JT columns) and direction
+    typedef SweepCfg<DK, JT, NS> SL;
+    constexpr size_t sweep_lds = SL::bytes;
     static bool sweep_attr_set = false;
     if (!sweep_attr_set) {
         hipError_t e0 = hipFuncSetAttribute((const void *)state_sweeps_kernel<DK, JT, TIn>,
@@ -905,7 +1013,7 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     sa.q = Lc.in.q; sa.k = Lc.in.k; sa.g = Lc.in.g; sa.tau = Lc.in.tau; sa.v = Lc.in.v; sa.beta = Lc.in.beta;
     sa.s0 = Lc.s0; sa.dout = Lc.dout; sa.dsf = Lc.dsf;
     sa.s_chunks = Lc.s_chunks; sa.s_final = Lc.s_final; sa.d_chunks = Lc.d_chunks; sa.ds0 = Lc.ds0;
-    hipLaunchKernelGGL((state_sweeps_kernel<DK, JT, TIn>), dim3(BH, DV / JT, 2), dim3(64 * SweepWaves<DK>::NW),
+    hipLaunchKernelGGL((state_sweeps_kernel<DK, JT, TIn>), dim3(BH, DV / JT, 2), dim3(SL::NT),
                        sweep_lds, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
