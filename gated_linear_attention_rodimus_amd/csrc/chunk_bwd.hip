@@ -41,6 +41,7 @@
 namespace rodimus {
 namespace bwd_detail {
 
+using chunk_detail::bf16x4;
 using chunk_detail::bf16x8;
 using chunk_detail::f32x4;
 using chunk_detail::kLog2e;
@@ -520,10 +521,78 @@ struct GradCfg {
     static constexpr size_t stage_v = (size_t)2 * C * OS * 4;             // at o_do
     static constexpr size_t need_v = o_do + stage_v;
     static constexpr size_t m01 = end3 > stage_k ? end3 : stage_k;
-    static constexpr size_t bytes = m01 > need_v ? m01 : need_v;
+    static constexpr size_t m02 = m01 > need_v ? m01 : need_v;
+    // raw bf16 gates q, k, g, tau [4][C][DK] staged for the transposing read:
+    // in phase A over the dO / V' planes (not yet written; past the f vector
+    // where those are small), in phase C over the Kt / Qt planes (no longer read)
+    static constexpr size_t gs_bytes = (size_t)4 * C * DK * 2;
+    static constexpr size_t o_gsa = o_do + gs_bytes <= o_f ? o_do : (end3 + 15) / 16 * 16;
+    static constexpr size_t o_gsc = 0;
+    static constexpr size_t bytes = m02 > o_gsa + gs_bytes ? m02 : o_gsa + gs_bytes;
+    static_assert(o_gsc + gs_bytes <= o_do, "phase C gate staging vs dA^T");
     // the f vector must survive the dv staging
     static_assert(o_f >= need_v || o_f + DK * 4 <= o_do, "f vs dv staging");
 };
+
+// Raw bf16 gates of the chunk through LDS: the whole [4][C][DK] block (q, k,
+// g, tau) is read by all threads with 16-byte loads, every load instruction
+// covering whole 128-byte rows, and stored row-major with the 16-byte pieces
+// of row u permuted by (u ^ u >> 2) (which spreads both the stores and the
+// transposing reads below over all banks); a state-row wave then reads its 16
+// columns in the MFMA C-layout with one transposing read per array and token
+// tile.
+template <int DK, int C>
+__device__ __forceinline__ int gate_slot(int u, int col) {
+    constexpr int PCH = DK / 8;
+    return u * DK + (((col >> 3) ^ ((u ^ (u >> 2)) & (PCH - 1))) << 3) + (col & 7);
+}
+
+template <int DK, int C, int NT>
+struct GateStage {
+    static constexpr int PCH = DK / 8, NPC = 4 * C * PCH, LPC = (NPC + NT - 1) / NT;
+    chunk_detail::u32x4 x[LPC];
+    // issue the loads (the array index is uniform over a wave: C * PCH is a
+    // multiple of 64)
+    __device__ __forceinline__ void load(const rsrc_t *R, unsigned HK, int tid) {
+#pragma unroll
+        for (int m = 0; m < LPC; ++m) {
+            const int p = tid + m * NT;
+            const int arr = __builtin_amdgcn_readfirstlane(p / (C * PCH));
+            const int u = (p / PCH) % C, c = p % PCH;
+            const rsrc_t Ra = arr == 0 ? R[0] : arr == 1 ? R[1] : arr == 2 ? R[2] : R[3];
+            x[m] = __builtin_amdgcn_raw_buffer_load_b128(Ra, p < NPC ? (u * HK + 8 * c) * 2u : 0x80000000u, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(__bf16 *dst, int tid) const {
+#pragma unroll
+        for (int m = 0; m < LPC; ++m) {
+            const int p = tid + m * NT;
+            if (p < NPC) {
+                const int arr = p / (C * PCH), u = (p / PCH) % C, c = p % PCH;
+                *(chunk_detail::u32x4 *)(dst + arr * C * DK + gate_slot<DK, C>(u, 8 * c)) = x[m];
+            }
+        }
+    }
+};
+
+// x_[arr][t][i] = gate arr at token 16 t + 4 lg + i, column 16 w + lc
+template <int DK, int C>
+__device__ __forceinline__ void read_gates(const __bf16 *src, int w, int lc, int lg, float (*q_)[4], float (*k_)[4],
+                                           float (*g_)[4], float (*t_)[4]) {
+    const int col = 16 * w + 4 * (lc & 3);
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) {
+        const int u = 16 * t + 4 * lg + (lc >> 2), o = gate_slot<DK, C>(u, col);
+        const bf16x4 a = chunk_detail::lds_read_tr(src + o);
+        const bf16x4 b = chunk_detail::lds_read_tr(src + C * DK + o);
+        const bf16x4 c = chunk_detail::lds_read_tr(src + 2 * C * DK + o);
+        const bf16x4 d = chunk_detail::lds_read_tr(src + 3 * C * DK + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q_[t][i] = (float)a[i]; k_[t][i] = (float)b[i]; g_[t][i] = (float)c[i]; t_[t][i] = (float)d[i];
+        }
+    }
+}
 
 // One workgroup per (b, h, chunk).  Roles of wave w:
 //   dk block w (w < DK/16): the gates of columns 16w..16w+15 over the chunk's
@@ -585,17 +654,29 @@ void chunk_grad_kernel(GradArgs a)
 
     // ---- phase A: gates of this wave's dk block, Qt and Kt into LDS (split);
     //      then A^T[s][u] = sum_r Kt[s][r] Qt[u][r] by token tiles, over Qt
+    constexpr bool kStageGates = !std::is_same<TIn, float>::value;
+    const rsrc_t Rgates[4] = {Rq, Rk, Rg, Rt};
+    if constexpr (kStageGates) {
+        GateStage<DK, C, NT> gs;
+        gs.load(Rgates, HK, tid);
+        gs.store((__bf16 *)(smem + L::o_gsa), tid);
+        __syncthreads();
+    }
     float d_[NU][4];                       // b - b_m (log2 units) at (token, r)
     float ebm = 0.f, fl = 0.f, ebl = 0.f;
     if (rwave) {
         float q_[NU][4], k_[NU][4], g_[NU][4], t_[NU][4];
+        if constexpr (kStageGates) {
+            read_gates<DK, C>((const __bf16 *)(smem + L::o_gsa), wave, lc, lg, q_, k_, g_, t_);
+        } else {
 #pragma unroll
-        for (int t = 0; t < NU; ++t)
+            for (int t = 0; t < NU; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
-                g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
+                    g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
+                }
+        }
         // b = inclusive cumulative sum of -g tau (log2 units): within the
         // lane's 4 tokens, across the 4 lane groups, then across token tiles
         float run = 0.f;
@@ -864,7 +945,10 @@ void chunk_grad_kernel(GradArgs a)
 
     // ---- phase C: dA^T into LDS (over dO), then dQt += dA Kt (s <= u) and
     //      dKt += dA^T Qt (u >= s) with Kt and Qt of the dk block as B operands
-    //      (gates reloaded: they are L2-resident by now)
+    //      (gates read again: bf16 through LDS, the block's Kt and Qt planes
+    //      being free; fp32 directly, from L2)
+    GateStage<DK, C, NT> gsc;
+    if constexpr (kStageGates) gsc.load(Rgates, HK, tid);
     if (wave < NU) {
         const int st = wave;
 #pragma unroll
@@ -881,14 +965,22 @@ void chunk_grad_kernel(GradArgs a)
     }
     float q_[NU][4], k_[NU][4], g_[NU][4], t_[NU][4], ah_[NU][4];
     float rs = 0.f;
+    if constexpr (kStageGates) {
+        gsc.store((__bf16 *)(smem + L::o_gsc), tid);
+        __syncthreads();
+    }
     if (rwave) {
+        if constexpr (kStageGates) {
+            read_gates<DK, C>((const __bf16 *)(smem + L::o_gsc), wave, lc, lg, q_, k_, g_, t_);
+        } else {
 #pragma unroll
-        for (int t = 0; t < NU; ++t)
+            for (int t = 0; t < NU; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
-                g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    q_[t][i] = gate(Rq, t, i); k_[t][i] = gate(Rk, t, i);
+                    g_[t][i] = gate(Rg, t, i); t_[t][i] = gate(Rt, t, i);
+                }
+        }
         // rowsum(S_o * D)_r = e^{b_L} sum_j S_in[r][j] D[r][j] + sum_s Kt[s][r] (f V' D^T)[s][r]
         // (S_o = diag(e^{b_L}) S_in + diag(f) Kt^T V'; dKt holds only its state term here)
         rs = ebl * sd;
@@ -902,7 +994,7 @@ void chunk_grad_kernel(GradArgs a)
         rs += __shfl_xor(rs, 16);
         rs += __shfl_xor(rs, 32);
     }
-    __syncthreads();
+    if constexpr (!kStageGates) __syncthreads();       // dA^T planes complete (else above)
     if (rwave) {
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
