@@ -497,9 +497,9 @@ __device__ __forceinline__ void sop_cols(const u16 *p0, int pl, int pitch, int c
 
 // LDS layout (bytes).  Split planes: Kt [C][DK]; Qt [C][DK], then A^T [C][C]
 // over it; one slab of JS dv columns of dO and V' [C][JS], then dA^T [C][C]
-// over dO.  The same area stages output rows as fp32: a slab of dv and
-// dbeta_hat [2][C][JS + 4] over the dO and V' planes, then dq, dk, dg, dtau
-// [4][C][DK + 4] over everything.
+// over dO.  The same area stages output rows as fp32: dV' of a slab
+// [C][JS + 4] over the dO and V' planes, then dq, dk, dg, dtau [4][C][DK + 4]
+// over everything.
 template <int DK, int DV, int NS>
 struct GradCfg {
     static constexpr int C = ChunkOf<DK>::C, NU = C / 16, NRB = DK / 16;
@@ -518,7 +518,7 @@ struct GradCfg {
     static constexpr size_t end3 = o_f + (size_t)DK * 4;
     static constexpr int OK = DK + 4, OS = JS + 4;                        // fp32 staging rows
     static constexpr size_t stage_k = (size_t)4 * C * OK * 4;             // at 0
-    static constexpr size_t stage_v = (size_t)2 * C * OS * 4;             // at o_do
+    static constexpr size_t stage_v = (size_t)C * OS * 4;                 // at o_do
     static constexpr size_t need_v = o_do + stage_v;
     static constexpr size_t m01 = end3 > stage_k ? end3 : stage_k;
     static constexpr size_t m02 = m01 > need_v ? m01 : need_v;
@@ -869,21 +869,33 @@ void chunk_grad_kernel(GradArgs a)
                 }
             }
         }
+        // v and beta_hat for dv = beta_hat dV' and dbeta_hat = v dV', read along
+        // rows 4 elements a lane for the row-store pass below (issued here so
+        // their latency passes under the dV' products)
+        constexpr int PRV = JS / 4, NPR = C * PRV, LPR = (NPR + NT - 1) / NT;
+        typedef typename std::conditional<std::is_same<TIn, float>::value, chunk_detail::u32x4,
+                                          unsigned __attribute__((ext_vector_type(2)))>::type Raw4;
+        Raw4 v4[LPR], b4[LPR];
+        {
+            const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ), Rb = make_rsrc(gb + bv, lim * DV * ESZ);
+#pragma unroll
+            for (int m = 0; m < LPR; ++m) {
+                const int p = tid + m * NT, u = p / PRV, j = (p % PRV) * 4;
+                const unsigned o = p < NPR ? (u * HV + j0 + j) * (unsigned)ESZ : 0x80000000u;
+                if constexpr (std::is_same<TIn, float>::value) {
+                    v4[m] = __builtin_amdgcn_raw_buffer_load_b128(Rv, o, 0, 0);
+                    b4[m] = __builtin_amdgcn_raw_buffer_load_b128(Rb, o, 0, 0);
+                } else {
+                    v4[m] = __builtin_amdgcn_raw_buffer_load_b64(Rv, o, 0, 0);
+                    b4[m] = __builtin_amdgcn_raw_buffer_load_b64(Rb, o, 0, 0);
+                }
+            }
+        }
         // dV' of this wave's dv tile of the slab
         f32x4 dvp[NU];
         const int jt = wave;                           // tile within the slab
         const int jg = j0 + 16 * jt + lc;              // this lane's dv column
-        Raw vr[NU][4], br[NU][4];
         if (jt < NJS) {
-            const rsrc_t Rv = make_rsrc(gv + bv, lim * DV * ESZ), Rb = make_rsrc(gb + bv, lim * DV * ESZ);
-#pragma unroll
-            for (int t = 0; t < NU; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const unsigned o = (16 * t + 4 * lg + i) * HV + jg;
-                    vr[t][i] = ld_raw<TIn>(Rv, o);
-                    br[t][i] = ld_raw<TIn>(Rb, o);
-                }
 #pragma unroll
             for (int t = 0; t < NU; ++t) dvp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -921,22 +933,33 @@ void chunk_grad_kernel(GradArgs a)
 #pragma unroll
             for (int t = 0; t < NU; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s_ = 16 * t + 4 * lg + i, j = 16 * jt + lc;
-                    sOutV[(0 * C + s_) * OS + j] = chunk_detail::in_to_f32(br[t][i]) * dvp[t][i];
-                    sOutV[(1 * C + s_) * OS + j] = chunk_detail::in_to_f32(vr[t][i]) * dvp[t][i];
-                }
+                for (int i = 0; i < 4; ++i) sOutV[(16 * t + 4 * lg + i) * OS + 16 * jt + lc] = dvp[t][i];
         __syncthreads();
         {
-            constexpr int PR = JS / 4, NP = 2 * C * PR, LP = (NP + NT - 1) / NT;
+            const rsrc_t Rdv = make_rsrc(a.dv + bv, lim * DV * 4), Rdb = make_rsrc(a.dbeta + bv, lim * DV * 4);
 #pragma unroll
-            for (int m = 0; m < LP; ++m) {
+            for (int m = 0; m < LPR; ++m) {
                 const int p = tid + m * NT;
-                if (p < NP) {
-                    const int o = p / (C * PR), u = (p / PR) % C, j = (p % PR) * 4;
-                    const rsrc_t R = make_rsrc((o == 0 ? a.dv : a.dbeta) + bv, lim * DV * 4);   // wave-uniform
-                    const chunk_detail::u32x4 x = *(const chunk_detail::u32x4 *)(sOutV + (o * C + u) * OS + j);
-                    __builtin_amdgcn_raw_buffer_store_b128(x, R, (u * HV + j0 + j) * 4u, 0, 2);
+                if (p < NPR) {
+                    const int u = p / PRV, j = (p % PRV) * 4;
+                    const f32x4 x = *(const f32x4 *)(sOutV + u * OS + j);
+                    f32x4 dvo, dbo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float ve, be;
+                        if constexpr (std::is_same<TIn, float>::value) {
+                            ve = __uint_as_float(v4[m][e]);
+                            be = __uint_as_float(b4[m][e]);
+                        } else {
+                            ve = __uint_as_float((e & 1) ? (v4[m][e >> 1] & 0xffff0000u) : (v4[m][e >> 1] << 16));
+                            be = __uint_as_float((e & 1) ? (b4[m][e >> 1] & 0xffff0000u) : (b4[m][e >> 1] << 16));
+                        }
+                        dvo[e] = be * x[e];
+                        dbo[e] = ve * x[e];
+                    }
+                    const unsigned o = (u * HV + j0 + j) * 4u;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(chunk_detail::u32x4, dvo), Rdv, o, 0, 2);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(chunk_detail::u32x4, dbo), Rdb, o, 0, 2);
                 }
             }
         }
