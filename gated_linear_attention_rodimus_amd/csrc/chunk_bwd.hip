@@ -456,7 +456,7 @@ typedef unsigned short u16;
 // The matrices the waves share go to LDS already split: NS planes of bf16
 // terms per matrix (plane n holds term n of every element), rows padded by 4
 // elements.  A row-wise MFMA operand is then two 8-byte reads per plane and no
-// arithmetic; a column-wise one is 8 two-byte reads per plane.
+// arithmetic; a column-wise one two transposing 8-byte reads per plane.
 template <int NS>
 __device__ __forceinline__ void split1(float x, u16 *t) {
     unsigned w[NS];
@@ -478,20 +478,18 @@ __device__ __forceinline__ void sop_rows(const u16 *p0, int pl, int pitch, int r
     }
 }
 
-// x[e] = element (k0 + kslot(lg, e), col)
+// x[e] = element (k0 + kslot(lg, e), col) for col = 16 tile + lc: two
+// transposing reads per plane (lane lc takes column col of tokens k0 + 4 lg
+// .. + 3 and k0 + 16 + 4 lg .. + 3, the k-slots of lane group lg)
 template <int NS, int K>
 __device__ __forceinline__ void sop_cols(const u16 *p0, int pl, int pitch, int col, int k0, int lg, bf16x8 *A) {
+    static_assert(K >= 32, "a column-wise operand spans a whole 32-deep step");
+    const int lc = col & 15;
+    const int row = k0 + 4 * lg + (lc >> 2), c4 = (col - lc) + 4 * (lc & 3);
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-        unsigned w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int e = 2 * e2;
-            const unsigned lo = (K >= 32 || e < 4) ? p0[n * pl + (k0 + kslot(lg, e)) * pitch + col] : 0u;
-            const unsigned hi = (K >= 32 || e < 4) ? p0[n * pl + (k0 + kslot(lg, e + 1)) * pitch + col] : 0u;
-            w[e2] = lo | (hi << 16);
-        }
-        A[n] = chunk_detail::pack8(w[0], w[1], w[2], w[3]);
+        const __bf16 *b = (const __bf16 *)(p0 + n * pl) + row * pitch + c4;
+        A[n] = chunk_detail::cat(chunk_detail::lds_read_tr(b), chunk_detail::lds_read_tr(b + 16 * pitch));
     }
 }
 
