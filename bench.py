@@ -75,7 +75,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled over steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--bwd-steps", type=int, default=5, help="timed backward calls (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=20, help="timed backward calls (0: skip)")
     ap.add_argument("--serve-steps", type=int, default=100,
                     help="decode steps after a long prefill (0: skip)")
     ap.add_argument("--serve-prefill", type=int, default=24576)
@@ -231,9 +231,11 @@ def main():
         bwsb = R.bwd_workspace_bytes(B, T, H, dk, dv)
         bws = torch.empty(max(bwsb, 1), dtype=torch.uint8, device=dev)
         t0_, s0_ = sets[0][0], sets[0][1]
-        for _ in range(2):
-            R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
-        torch.cuda.synchronize()
+        tw = time.perf_counter()                 # warm-up: 50 ms of this call
+        while time.perf_counter() - tw < 0.05:
+            for _ in range(2):
+                R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.bwd_steps):
