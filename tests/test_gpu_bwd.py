@@ -113,6 +113,19 @@ def test_bwd_gate_edges(R, dev):
     check(R, dev, x, d_out, d_sf, None, BAR["f32"])
 
 
+def test_bwd_gate_edges_bf16(R, dev):
+    """The same edges at the production shape (dk 64, dv 128, bf16 inputs), where
+    the sweeps fold g^tau into one exponent and the gradient kernel stages the
+    gates through LDS: g = 0, tau = 0 and both (0^0 = 1) on separate columns."""
+    x = D.make("layer130m", B=1, T=100, H=2)
+    x.g[:, :, 0, :4] = 0
+    x.tau[:, :, 1, 4:8] = 0
+    x.g[:, :50, :, 8:10] = 0
+    x.tau[:, :50, :, 8:10] = 0
+    d_out, d_sf = cotangents(x, 15)
+    check(R, dev, x, d_out, d_sf, None, BAR["bf16"])
+
+
 def test_bwd_no_tokens(R, dev):
     x = D.make("tiny", T=0)
     d_out, d_sf = cotangents(x, 13)
