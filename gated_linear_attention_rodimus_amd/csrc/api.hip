@@ -72,7 +72,16 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     // drop empty trailing segments
     if (P->chunks_per_seg > 0) seg = (P->n_chunks + P->chunks_per_seg - 1) / P->chunks_per_seg;
     P->segments = seg;
-    P->ws_bytes = seg > 1 ? (size_t)B * H * seg * ((size_t)dk * dv + dk) * sizeof(float) : 0;
+    // the transfers cover the segments before the last (the output pass of
+    // the last one writes S_T from its true incoming state); each is cut into
+    // 2 pieces where that still fits one workgroup per CU (measured: 1.6B
+    // layer, 64 heads x 2 tiles x 2 segments, 180 -> 153 us)
+    const long long units = heads * (dv / dvt);
+    P->tr_per_seg = 1;
+    if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= kTargetBlocks) P->tr_per_seg = 2;
+    const int tr = (seg - 1) * P->tr_per_seg;
+    P->ws_slots = seg > tr ? seg : tr;
+    P->ws_bytes = seg > 1 ? (size_t)B * H * P->ws_slots * ((size_t)dk * dv + dk) * sizeof(float) : 0;
     return true;
 }
 
@@ -197,6 +206,7 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
     Lc.f32_inputs = f32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.gam_out = nullptr;
+    Lc.gam_bh_stride = 0;
     const long long sz = (long long)dk * dv;
     if (P.segments == 1) {
         Lc.n_seg = 1; Lc.mode = 0;
@@ -207,24 +217,25 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
         e = launch_chunk(Lc, stream);
         return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
     }
-    // segmented: (1) per-segment transfers from a zero state, (2) ordered
-    // combination into each segment's incoming state, (3) outputs.
-    const int n_seg = P.segments;
-    float *ws_ds = (float *)workspace;                                // [BH][P][dk][dv]
-    float *ws_gam = ws_ds + (size_t)B * H * n_seg * dk * dv;          // [BH][P][dk]
-    Lc.n_seg = n_seg; Lc.mode = 1;
+    // segmented: (1) transfers from a zero state over the chunks before the
+    // last segment, tr_per_seg pieces per segment, (2) ordered combination into
+    // each segment's incoming state, (3) outputs (the last segment's also
+    // writes S_T).
+    const int n_seg = P.segments, per = P.tr_per_seg, slots = P.ws_slots;
+    float *ws_ds = (float *)workspace;                                // [BH][slots][dk][dv]
+    float *ws_gam = ws_ds + (size_t)B * H * slots * dk * dv;          // [BH][slots][dk]
+    Lc.n_seg = (n_seg - 1) * per; Lc.chunks_per_seg = P.chunks_per_seg / per; Lc.mode = 1;
     Lc.s_in = nullptr; Lc.s_in_bh_stride = 0; Lc.s_in_seg_stride = 0;
     Lc.out = nullptr;
-    Lc.s_out = ws_ds; Lc.s_out_bh_stride = (long long)n_seg * sz; Lc.s_out_seg_stride = sz;
+    Lc.s_out = ws_ds; Lc.s_out_bh_stride = (long long)slots * sz; Lc.s_out_seg_stride = sz;
     Lc.s_out_last_only = 0;
-    Lc.gam_out = ws_gam;
+    Lc.gam_out = ws_gam; Lc.gam_bh_stride = (long long)slots * dk;
     e = launch_chunk(Lc, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
-    // final state: the output pass's last segment writes it (from its true S_in)
-    e = launch_segment_combine(B * H, n_seg, dk, dv, initial_state, ws_ds, ws_gam, nullptr, stream);
+    e = launch_segment_combine(B * H, n_seg, per, slots, dk, dv, initial_state, ws_ds, ws_gam, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
-    Lc.mode = 0;
-    Lc.s_in = ws_ds; Lc.s_in_bh_stride = (long long)n_seg * sz; Lc.s_in_seg_stride = sz;
+    Lc.n_seg = n_seg; Lc.chunks_per_seg = P.chunks_per_seg; Lc.mode = 0;
+    Lc.s_in = ws_ds; Lc.s_in_bh_stride = (long long)slots * sz; Lc.s_in_seg_stride = sz;
     Lc.out = out;
     Lc.s_out = final_state; Lc.s_out_bh_stride = sz; Lc.s_out_seg_stride = 0;
     Lc.s_out_last_only = 1;

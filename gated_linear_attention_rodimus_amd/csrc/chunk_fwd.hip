@@ -27,11 +27,13 @@ hipError_t launch_chunk_dk128(const ChunkLaunch &, hipStream_t);
 namespace {
 
 // ---------------------------------------------------------------- segment combine
-// S_in[0] = S0 (or 0); S_in[p] = diag(gam[p-1]) S_in[p-1] + dS[p-1]; written in
-// place over dS.  One thread per state element, sequential over segments.
+// S_in[0] = S0 (or 0); S_in[p + 1] = the transfers p * per .. p * per + per - 1
+// applied in order to S_in[p] (each: S <- diag(gam[j]) S + dS[j]); S_in[p] is
+// written to slot p, after every transfer in that slot has been read.  One
+// thread per state element, sequential over segments.
 __global__ __launch_bounds__(256) void segment_combine_kernel(
-    int n_seg, int dk, int dv, const float *__restrict__ s0, float *__restrict__ ds,
-    const float *__restrict__ gam, float *__restrict__ final_state)
+    int n_seg, int per, int slots, int dk, int dv, const float *__restrict__ s0,
+    float *__restrict__ ds, const float *__restrict__ gam)
 {
     const int bh = blockIdx.y;
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -39,14 +41,17 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(
     const int i = e / dv;
     const size_t st = (size_t)dk * dv;
     float run = s0 ? s0[(size_t)bh * st + e] : 0.f;
-    float *d = ds + (size_t)bh * n_seg * st + e;
-    const float *gm = gam + (size_t)bh * n_seg * dk + i;
+    float *d = ds + (size_t)bh * slots * st + e;
+    const float *gm = gam + (size_t)bh * slots * dk + i;
     for (int p = 0; p < n_seg; ++p) {
-        const float dsp = d[(size_t)p * st];
-        d[(size_t)p * st] = run;
-        run = gm[(size_t)p * dk] * run + dsp;
+        const float cur = run;
+        if (p + 1 < n_seg)
+            for (int f = 0; f < per; ++f) {
+                const int j = p * per + f;
+                run = gm[(size_t)j * dk] * run + d[(size_t)j * st];
+            }
+        d[(size_t)p * st] = cur;
     }
-    if (final_state) final_state[(size_t)bh * st + e] = run;
 }
 
 __global__ __launch_bounds__(256) void state_copy_kernel(const float *__restrict__ src,
@@ -80,14 +85,14 @@ hipError_t launch_chunk(const ChunkLaunch &Lc, hipStream_t stream)
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_segment_combine(int BH, int n_seg, int dk, int dv, const float *s0,
-                                  float *ds_inout, const float *gam, float *final_state,
+hipError_t launch_segment_combine(int BH, int n_seg, int per, int slots, int dk, int dv,
+                                  const float *s0, float *ds_inout, const float *gam,
                                   hipStream_t stream)
 {
     const int elems = dk * dv;
     dim3 grid((elems + 255) / 256, BH);
-    hipLaunchKernelGGL(segment_combine_kernel, grid, dim3(256), 0, stream, n_seg, dk, dv, s0,
-                       ds_inout, gam, final_state);
+    hipLaunchKernelGGL(segment_combine_kernel, grid, dim3(256), 0, stream, n_seg, per, slots, dk,
+                       dv, s0, ds_inout, gam);
     return hipGetLastError();
 }
 

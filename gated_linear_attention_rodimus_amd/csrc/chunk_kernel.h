@@ -239,7 +239,7 @@ struct Args {
     const float *s_in; long long s_in_bh, s_in_seg;
     float *out;
     float *s_out; long long s_out_bh, s_out_seg; int s_out_last_only;
-    float *gam_out;
+    float *gam_out; long long gam_bh;   // segment decays (mode 1): head bh, segment p at bh * gam_bh + p * DK
     int remap;                   // XCD-aware block mapping on/off
 };
 
@@ -560,7 +560,7 @@ __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(
             if (it + 1 <= c_end) iter(it + 1, std::integral_constant<int, 1>());
         }
         if (!outputs && a.gam_out && jt == 0 && prep && cgp == 0)
-            *(float2 *)(a.gam_out + ((size_t)bh * a.n_seg + seg) * DK + c0) =
+            *(float2 *)(a.gam_out + (size_t)bh * a.gam_bh + (size_t)seg * DK + c0) =
                 make_float2(gam_acc0, gam_acc1);
         return;
     }
@@ -851,7 +851,7 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     a.out = Lc.out;
     a.s_out = Lc.s_out; a.s_out_bh = Lc.s_out_bh_stride; a.s_out_seg = Lc.s_out_seg_stride;
     a.s_out_last_only = Lc.s_out_last_only;
-    a.gam_out = Lc.gam_out;
+    a.gam_out = Lc.gam_out; a.gam_bh = Lc.gam_bh_stride;
     const long long blocks = (long long)Lc.B * Lc.H * Lc.n_seg * a.n_jt;
     a.remap = (blocks % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn, OUT>), dim3((unsigned)blocks), dim3(L::NT),

@@ -20,6 +20,10 @@ struct ChunkPlan {
     int segments;   // pieces per (b, h) sequence run in parallel (1 = one sweep)
     int n_chunks;   // ceil(T / C)
     int chunks_per_seg;
+    // segmented runs: transfers over the chunks before the last segment, in
+    // tr_per_seg pieces per segment (tr_per_seg * (segments - 1) of them)
+    int tr_per_seg;
+    int ws_slots;   // state slots per (b, h) in the workspace
     size_t lds_bytes;
     size_t ws_bytes;
 };
@@ -38,14 +42,16 @@ struct ChunkLaunch {
     const float *s_in; long long s_in_bh_stride, s_in_seg_stride;
     float *out;
     float *s_out; long long s_out_bh_stride, s_out_seg_stride; int s_out_last_only;
-    float *gam_out;         // [B*H][n_seg][dk] (mode 1)
+    float *gam_out;         // mode 1: segment p's decay of head bh at bh * gam_bh_stride + p * dk
+    long long gam_bh_stride;
 };
 hipError_t launch_chunk(const ChunkLaunch &L, hipStream_t stream);
 
-// Ordered combination of segment transfers: S_in[p] for every segment, in
-// place over dS, plus optionally the final state.
-hipError_t launch_segment_combine(int BH, int n_seg, int dk, int dv, const float *s0,
-                                  float *ds_inout, const float *gam, float *final_state,
+// Ordered combination of segment transfers: S_in[p] of every segment, in
+// place over the transfers (per transfers for each segment but the last;
+// slots state slots per head).
+hipError_t launch_segment_combine(int BH, int n_seg, int per, int slots, int dk, int dv,
+                                  const float *s0, float *ds_inout, const float *gam,
                                   hipStream_t stream);
 
 // Copy or zero a [count] fp32 array (T == 0 forwards).
