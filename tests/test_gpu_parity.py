@@ -138,6 +138,39 @@ def test_decode_batch_1000_steps(R, dev):
     assert e <= 1e-2
 
 
+def run_decode_steps(R, dev, x, s0, steps):
+    """decode_step token by token against the oracle's decode; returns the worst
+    output error and the final-state error."""
+    t = to_dev(x, dev)
+    S = torch.from_numpy(np.ascontiguousarray(s0, np.float32)).to(dev)
+    Sref = s0.astype(np.float64)
+    worst = 0.0
+    for s in range(steps):
+        o = R.decode_step(*(a[:, s].contiguous() for a in t), S)
+        ro, Sref = oracle.decode(*(np.ascontiguousarray(x.f32(n)[:, s]) for n in NAMES), Sref)
+        worst = max(worst, err(o.cpu().numpy(), ro))
+    return worst, err(S.cpu().numpy(), Sref)
+
+
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_decode_all_widths_bf16(R, dev, dk, dv):
+    """Decode steps at every width: 5 sequences x 3 heads, so the small heads,
+    several state slices to a workgroup, end on a partly filled workgroup."""
+    x = D.make("layer1p6b", B=5, T=6, H=3, dk=dk, dv=dv)
+    s0 = D.make("long_prefill", B=5, T=1, H=3, dk=dk, dv=dv).initial_state
+    eo, es = run_decode_steps(R, dev, x, s0, 6)
+    assert eo <= BAR["bf16"] and es <= BAR["bf16"], (eo, es)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 128), (128, 32)])
+def test_decode_fp32_inputs(R, dev, dk, dv):
+    x = D.make("tiny", B=5, T=6, H=3, dk=dk, dv=dv)
+    s0 = D.make("long_prefill", B=5, T=1, H=3, dk=dk, dv=dv).initial_state
+    eo, es = run_decode_steps(R, dev, x, s0, 6)
+    assert eo <= BAR["f32"] and es <= BAR["f32"], (eo, es)
+
+
 # ---------------------------------------------------------------- shapes, chunking, paths
 
 
