@@ -293,17 +293,24 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-        # bounded sample: all heads of the first sequences, whole length
+        # sample: the whole batch (all sequences and heads, whole length), in
+        # repeated passes until about 10 s of CPU work have been timed
         Bs = B
         ins = [np.ascontiguousarray(x.f32(n)[:Bs]) for n in NAMES]
         s0 = None if x.initial_state is None else x.initial_state[:Bs]
+        passes = 0
         c0 = time.perf_counter()
-        ro, _ = oracle.fwd(*ins, s0, nthreads=nthreads)
+        ro = None
+        while passes == 0 or time.perf_counter() - c0 < 10.0:
+            o_, _ = oracle.fwd(*ins, s0, nthreads=nthreads)
+            if ro is None:
+                ro = o_
+            passes += 1
         cs = time.perf_counter() - c0
-        cpu = {"value": round(Bs * T / cs, 1), "unit": "tokens/s", "cores": oracle.fwd.last_threads,
-               "kind": "oracle",
+        cpu = {"value": round(passes * Bs * T / cs, 1), "unit": "tokens/s",
+               "cores": oracle.fwd.last_threads, "kind": "oracle",
                "sample": f"{Bs} of {B} sequences x {T} tokens x {H} heads of the same workload, "
-                         f"fp64 C oracle, {cs:.2f} s"}
+                         f"{passes} passes, fp64 C oracle, {cs:.1f} s"}
         gpu_o = sets[0][2][:Bs].cpu().numpy()
         parity = {"max_abs_over_rms": oracle.rel_to_rms_error(gpu_o, ro), "bar": 1e-2,
                   "sample": "the CPU-baseline sample"}
