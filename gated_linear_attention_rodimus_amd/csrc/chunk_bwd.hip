@@ -599,7 +599,10 @@ __device__ __forceinline__ void read_gates(const __bf16 *src, int w, int lc, int
 //     t = 2 ks, 2 ks + 1, the k-slots of step ks), then dQt and dKt of the block
 //     and the elementwise tail (dq, dk, dlambda, dg, dtau);
 //   token tile w (w < C/16): rows w of A^T and dA^T;
-//   dv tile w of each slab: dV' of those 16 columns, then dv and dbeta_hat.
+//   dv tile w of each slab: dV' of those 16 columns (every thread then forms
+//     dv and dbeta_hat from it in the slab's row-store pass).
+// bf16 gates reach the dk blocks through LDS (whole-row loads by all threads,
+// transposing reads), once for Qt / Kt and again for the elementwise tail.
 // The dv slabs are processed one after the other (dA^T, dQt and dKt
 // accumulate over them), which keeps the LDS small enough for two workgroups
 // per CU: one computes while the other waits for memory.
