@@ -108,8 +108,9 @@ template <> struct Pair<__bf16> {
     }
     static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x << 16); }
     static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x & 0xffff0000u); }
-    // run + g * t of the low / high elements (one packed dot product each; the
-    // operands are the unpacked words, i.e. pairs (0, x))
+    // run + g * t of the low / high elements: one packed dot product each, with
+    // the other element of t masked to zero (the gates are finite, so the
+    // masked product is an exact zero)
     static __device__ __forceinline__ float gt_lo(type g, type t, float run) {
         return dot2_bf16(g << 16, t << 16, run);
     }
@@ -243,10 +244,14 @@ struct Args {
     int remap;                   // XCD-aware block mapping on/off
 };
 
+// v_mul_legacy_f32: an IEEE product, except that 0 times anything (infinities
+// included) is 0.
+__device__ float fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
+
 // log2 of alpha_hat = g^tau: tau * log2(g), and exactly 0 when tau == 0 (g^0 = 1,
-// also at g = 0 where log2(g) = -inf).
+// also at g = 0 where log2(g) = -inf); -inf for g = 0 < tau.
 __device__ __forceinline__ float log2_gate_pow(float g, float tau) {
-    return tau == 0.f ? 0.f : tau * __builtin_amdgcn_logf(g);
+    return fmul_legacy(tau, __builtin_amdgcn_logf(g));
 }
 
 // Transposed LDS read of a 16-bit operand (gfx950 ds_read_b64_tr_b16).  Within
