@@ -74,11 +74,16 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     P->segments = seg;
     // the transfers cover the segments before the last (the output pass of
     // the last one writes S_T from its true incoming state); each is cut into
-    // 2 pieces where that still fits one workgroup per CU (measured: 1.6B
-    // layer, 64 heads x 2 tiles x 2 segments, 180 -> 153 us)
+    // 2 pieces where they all still run at once (measured: 1.6B layer, 64
+    // heads x 2 tiles x 2 segments, 180 -> 153 us), and into 4 pieces of at
+    // least 8 chunks where the CUs hold that many transfer workgroups
     const long long units = heads * (dv / dvt);
+    const long long xfer_cap = (long long)kTargetBlocks * chunk_xfer_per_cu(dk, dvt, P->C, f32);
     P->tr_per_seg = 1;
-    if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= kTargetBlocks) P->tr_per_seg = 2;
+    if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= xfer_cap) P->tr_per_seg = 2;
+    if (seg > 1 && P->chunks_per_seg % 4 == 0 && P->chunks_per_seg / 4 >= 8 &&
+        units * (seg - 1) * 4 <= xfer_cap)
+        P->tr_per_seg = 4;
     const int tr = (seg - 1) * P->tr_per_seg;
     P->ws_slots = seg > tr ? seg : tr;
     P->ws_bytes = seg > 1 ? (size_t)B * H * P->ws_slots * ((size_t)dk * dv + dk) * sizeof(float) : 0;

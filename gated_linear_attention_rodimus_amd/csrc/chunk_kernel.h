@@ -265,10 +265,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Compile-time shape of one instantiation, and its LDS layout (bytes).
-template <int DK, int DVT, int C, int NS_>
+// Compile-time shape of one instantiation, and its LDS layout (bytes).  The
+// segment-transfer mode (OUT_ false) keeps no Qt planes, score tiles or
+// output tile.
+template <int DK, int DVT, int C, int NS_, bool OUT_ = true>
 struct Cfg {
     static constexpr int NS = NS_;
+    static constexpr bool OUT = OUT_;
     static constexpr int NP = 4;                              // producer waves
     static constexpr int NJ = DVT / 16;                       // consumer waves
     static constexpr int NW = NP + NJ;
@@ -285,13 +288,13 @@ struct Cfg {
     static constexpr int MID = C / 2 - 1;                     // reference token b_m
     // one pipeline buffer: Qt and Kt planes, exp(b_m), exp(b_L), exp(b_L - b_m)
     static constexpr size_t bq_off = 0;
-    static constexpr size_t bk_off = bq_off + (size_t)NS * C * RS * 2;
+    static constexpr size_t bk_off = bq_off + (OUT ? (size_t)NS * C * RS * 2 : 0);
     static constexpr size_t bem_off = bk_off + (size_t)NS * C * RS * 2;
     static constexpr size_t bgam_off = bem_off + (size_t)DK * 4;
     static constexpr size_t bgm_off = bgam_off + (size_t)DK * 4;
     static constexpr size_t buf_bytes = (bgm_off + (size_t)DK * 4 + 15) / 16 * 16;
     static constexpr size_t a_off = 2 * buf_bytes;
-    static constexpr size_t tot_off = a_off + (size_t)NA * NS * 64 * 4 * 2;
+    static constexpr size_t tot_off = a_off + (OUT ? (size_t)NA * NS * 64 * 4 * 2 : 0);
     static constexpr size_t mid_off = tot_off + (size_t)NG * DK * 4;
     // per consumer wave: raw v and beta_hat of one chunk, [C][16] bf16 each
     static constexpr size_t stg_off = mid_off + (size_t)DK * 4;
@@ -300,16 +303,23 @@ struct Cfg {
     // four row groups of an MFMA C-layout write land in distinct banks)
     static constexpr int OS = DVT + 16;
     static constexpr size_t out_off = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
-    static constexpr size_t bytes = out_off + (size_t)C * OS * 4;
+    static constexpr size_t bytes = out_off + (OUT ? (size_t)C * OS * 4 : 0);
+    // workgroups per CU the kernel is compiled for: two for the bf16 transfer
+    // mode where two fit the CU's LDS and four waves per SIMD leave each wave
+    // enough registers (128) without spilling; one otherwise
+    static constexpr int per_cu = (!OUT && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64) ? 2 : 1;
+    static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
 
 template <int DK, int DVT, int C, typename TIn, bool OUT>
-__global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT), 1) void chunk_fwd_kernel(Args a)
+__global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT),
+                             (Cfg<DK, DVT, C, std::is_same<TIn, float>::value ? 3 : 2, OUT>::waves_per_eu))
+void chunk_fwd_kernel(Args a)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    typedef Cfg<DK, DVT, C, NS> L;
+    typedef Cfg<DK, DVT, C, NS, OUT> L;
     typedef typename InRaw<TIn>::type Raw;
     typedef Pair<TIn> PR;
     typedef typename PR::type Raw2;
@@ -836,7 +846,7 @@ template <int DK, int DVT, int C, typename TIn, bool OUT>
 hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    typedef Cfg<DK, DVT, C, NS> L;
+    typedef Cfg<DK, DVT, C, NS, OUT> L;
     const size_t lds = L::bytes;
     static bool attr_set = false;
     if (!attr_set) {
@@ -876,6 +886,10 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 #define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC)                                            \
     if (dvt == XV && C == XC)                                                         \
         return f32 ? chunk_detail::Cfg<XK, XV, XC, 3>::bytes : chunk_detail::Cfg<XK, XV, XC, 2>::bytes;
+#define RODIMUS_CHUNK_CASE_PCU(XK, XV, XC)                                            \
+    if (dvt == XV && C == XC)                                                         \
+        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3, false>::per_cu                  \
+                   : chunk_detail::Cfg<XK, XV, XC, 2, false>::per_cu;
 #define RODIMUS_CHUNK_CASE_LAUNCH(XK, XV, XC)                                         \
     if (Lc.DVT == XV && Lc.C == XC)                                                   \
         return Lc.f32_inputs ? chunk_detail::launch_t<XK, XV, XC, float>(Lc, stream)  \
@@ -889,6 +903,11 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
     {                                                                                 \
         RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LDS, XK)                              \
         return 0;                                                                     \
+    }                                                                                 \
+    int chunk_xfer_per_cu_dk##XK(int dvt, int C, bool f32)                            \
+    {                                                                                 \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_PCU, XK)                              \
+        return 1;                                                                     \
     }                                                                                 \
     hipError_t launch_chunk_dk##XK(const ChunkLaunch &Lc, hipStream_t stream)         \
     {                                                                                 \

@@ -209,6 +209,15 @@ def test_segmented_path(R, dev, segments):
     check_full(R, x, dev, s0=x.initial_state, segments=segments, label=f"segments {segments}")
 
 
+@pytest.mark.parametrize("T,segments", [(4096, 2), (6144, 3), (94 * 64 + 37, 3)])
+def test_segmented_transfers_in_four_pieces(R, dev, T, segments):
+    # 32 chunks per segment: each transfer before the last segment is cut
+    # into 4 pieces of 8 chunks (bf16 transfers run two workgroups per CU);
+    # the last case ends in a shorter segment with a ragged last chunk
+    x = D.make("long_prefill", B=1, T=T, H=2)
+    check_full(R, x, dev, s0=x.initial_state, segments=segments, label=f"T {T} segments {segments}")
+
+
 def test_split_sequence_carry_over(R, dev):
     x = D.make("layer1p6b", B=2, T=700, H=3)
     ro, rs = ref(x)
