@@ -47,22 +47,35 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
         found = true;
     }
     if (!found) return false;
-    P->n_chunks = T > 0 ? (T + P->C - 1) / P->C : 0;
     const long long heads = (long long)B * H;
-    int dvt = dv < 64 ? dv : 64;
+    const int dvt = dv < 64 ? dv : 64;
+    const long long units = heads * (dv / dvt);
     int seg = segments;
     if (seg == 0) {
         seg = 1;
         // one sweep per (b, h, dv tile) while that fills more than half the
-        // CUs; at half or fewer, split the sequences into segments (measured:
-        // 64 heads x 2 tiles over 64 chunks, 2 segments ~5 % faster)
-        if (heads * (dv / dvt) <= kTargetBlocks / 2 && P->n_chunks >= 16) {
-            long long want = kTargetBlocks / (heads * (dv / dvt));
-            long long cap = P->n_chunks / 8;
-            seg = (int)(want < cap ? want : cap);
-            if (seg < 1) seg = 1;
+        // CUs; at half or fewer, split the sequences into segments of at least
+        // 8 chunks, as many as run at once.  Chunks of 32 tokens are taken
+        // there when that kernel holds two workgroups per CU (twice the
+        // segments; measured: long prefill, 16 heads x 2 tiles, 16 segments
+        // of C = 32 584 us against 8 of C = 64 630 us; 1.6B layer, 64 heads x
+        // 2 tiles, 4 of C = 32 142 us against 2 of C = 64 151 us)
+        if (units <= kTargetBlocks / 2) {
+            int Cs = P->C;
+            if (P->C > 32 && chunk_per_cu(dk, dvt, 32, f32, true) == 2 &&
+                chunk_lds_bytes(dk, dvt, 32, f32) != 0)
+                Cs = 32;
+            const long long nch = T > 0 ? (T + Cs - 1) / Cs : 0;
+            if (nch >= 16) {
+                long long want = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, Cs, f32, true) / units;
+                long long cap = nch / 8;
+                seg = (int)(want < cap ? want : cap);
+                if (seg < 1) seg = 1;
+                if (seg > 1) P->C = Cs;
+            }
         }
     }
+    P->n_chunks = T > 0 ? (T + P->C - 1) / P->C : 0;
     P->DVT = dvt;
     P->lds_bytes = chunk_lds_bytes(dk, dvt, P->C, f32);
     if (P->lds_bytes == 0 || P->lds_bytes > kLdsLimit) return false;
@@ -75,10 +88,10 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     // the transfers cover the segments before the last (the output pass of
     // the last one writes S_T from its true incoming state); each is cut into
     // 2 pieces where they all still run at once (measured: 1.6B layer, 64
-    // heads x 2 tiles x 2 segments, 180 -> 153 us), and into 4 pieces of at
-    // least 8 chunks where the CUs hold that many transfer workgroups
-    const long long units = heads * (dv / dvt);
-    const long long xfer_cap = (long long)kTargetBlocks * chunk_xfer_per_cu(dk, dvt, P->C, f32);
+    // heads x 2 tiles x 2 segments of C = 64, 180 -> 153 us), and into 4
+    // pieces of at least 8 chunks where the CUs hold that many transfer
+    // workgroups
+    const long long xfer_cap = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, P->C, f32, false);
     P->tr_per_seg = 1;
     if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= xfer_cap) P->tr_per_seg = 2;
     if (seg > 1 && P->chunks_per_seg % 4 == 0 && P->chunks_per_seg / 4 >= 8 &&

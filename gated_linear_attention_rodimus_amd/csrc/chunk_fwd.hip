@@ -19,10 +19,10 @@ size_t chunk_lds_bytes_dk16(int, int, bool);
 size_t chunk_lds_bytes_dk32(int, int, bool);
 size_t chunk_lds_bytes_dk64(int, int, bool);
 size_t chunk_lds_bytes_dk128(int, int, bool);
-int chunk_xfer_per_cu_dk16(int, int, bool);
-int chunk_xfer_per_cu_dk32(int, int, bool);
-int chunk_xfer_per_cu_dk64(int, int, bool);
-int chunk_xfer_per_cu_dk128(int, int, bool);
+int chunk_per_cu_dk16(int, int, bool, bool);
+int chunk_per_cu_dk32(int, int, bool, bool);
+int chunk_per_cu_dk64(int, int, bool, bool);
+int chunk_per_cu_dk128(int, int, bool, bool);
 hipError_t launch_chunk_dk16(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk32(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk64(const ChunkLaunch &, hipStream_t);
@@ -78,13 +78,13 @@ size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs)
     return 0;
 }
 
-int chunk_xfer_per_cu(int dk, int dvt, int C, bool f32_inputs)
+int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs)
 {
     switch (dk) {
-    case 16: return chunk_xfer_per_cu_dk16(dvt, C, f32_inputs);
-    case 32: return chunk_xfer_per_cu_dk32(dvt, C, f32_inputs);
-    case 64: return chunk_xfer_per_cu_dk64(dvt, C, f32_inputs);
-    case 128: return chunk_xfer_per_cu_dk128(dvt, C, f32_inputs);
+    case 16: return chunk_per_cu_dk16(dvt, C, f32_inputs, outputs);
+    case 32: return chunk_per_cu_dk32(dvt, C, f32_inputs, outputs);
+    case 64: return chunk_per_cu_dk64(dvt, C, f32_inputs, outputs);
+    case 128: return chunk_per_cu_dk128(dvt, C, f32_inputs, outputs);
     }
     return 1;
 }

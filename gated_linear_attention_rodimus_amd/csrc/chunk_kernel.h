@@ -304,10 +304,12 @@ struct Cfg {
     static constexpr int OS = DVT + 16;
     static constexpr size_t out_off = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
     static constexpr size_t bytes = out_off + (OUT ? (size_t)C * OS * 4 : 0);
-    // workgroups per CU the kernel is compiled for: two for the bf16 transfer
-    // mode where two fit the CU's LDS and four waves per SIMD leave each wave
-    // enough registers (128) without spilling; one otherwise
-    static constexpr int per_cu = (!OUT && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64) ? 2 : 1;
+    // workgroups per CU the kernel is compiled for: two for bf16 inputs at
+    // dk <= 64 in the transfer mode, and in the output mode at C <= 32, where
+    // two fit the CU's LDS and four waves per SIMD leave each wave enough
+    // registers (128) without spilling; one otherwise
+    static constexpr int per_cu =
+        ((!OUT || C <= 32) && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
@@ -888,8 +890,10 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
         return f32 ? chunk_detail::Cfg<XK, XV, XC, 3>::bytes : chunk_detail::Cfg<XK, XV, XC, 2>::bytes;
 #define RODIMUS_CHUNK_CASE_PCU(XK, XV, XC)                                            \
     if (dvt == XV && C == XC)                                                         \
-        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3, false>::per_cu                  \
-                   : chunk_detail::Cfg<XK, XV, XC, 2, false>::per_cu;
+        return outputs ? (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true>::per_cu        \
+                              : chunk_detail::Cfg<XK, XV, XC, 2, true>::per_cu)       \
+                       : (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, false>::per_cu       \
+                              : chunk_detail::Cfg<XK, XV, XC, 2, false>::per_cu);
 #define RODIMUS_CHUNK_CASE_LAUNCH(XK, XV, XC)                                         \
     if (Lc.DVT == XV && Lc.C == XC)                                                   \
         return Lc.f32_inputs ? chunk_detail::launch_t<XK, XV, XC, float>(Lc, stream)  \
@@ -904,7 +908,7 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
         RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LDS, XK)                              \
         return 0;                                                                     \
     }                                                                                 \
-    int chunk_xfer_per_cu_dk##XK(int dvt, int C, bool f32)                            \
+    int chunk_per_cu_dk##XK(int dvt, int C, bool f32, bool outputs)                   \
     {                                                                                 \
         RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_PCU, XK)                              \
         return 1;                                                                     \

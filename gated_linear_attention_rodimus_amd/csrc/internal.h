@@ -30,8 +30,9 @@ struct ChunkPlan {
 
 // Bytes of LDS the chunk kernel needs for a tile shape (0 if not instantiated).
 size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs);
-// Workgroups of the segment-transfer mode one CU holds for a tile shape.
-int chunk_xfer_per_cu(int dk, int dvt, int C, bool f32_inputs);
+// Workgroups of the output mode (outputs true) or of the segment-transfer
+// mode one CU holds for a tile shape.
+int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs);
 
 // Chunk sweep / segment pass.  mode 0: outputs from S_in; mode 1: segment
 // state transfer (dS from a zero state, and the product of decays).

@@ -112,10 +112,12 @@ def test_chunk_workspace_required_for_segments():
 def test_workspace_bytes_plan():
     # one sweep when the (b, h, dv tile) units fill more than half the CUs: no workspace
     assert R.workspace_bytes(8, 2048, 12, 64, 128) == 0
-    # 64 heads x 2 dv tiles = half the CUs: two segments; the first one's
-    # transfer is cut into 4 pieces of 8 chunks (bf16 transfers run two
-    # workgroups per CU, so 512 of them run at once): 4 slots per head
+    # 64 heads x 2 dv tiles = half the CUs: segmented.  bf16 inputs: chunks of
+    # 32 tokens, whose kernels hold two workgroups per CU, so 4 segments (512
+    # workgroups) and 3 transfers; fp32 inputs: 2 segments of 64-token chunks,
+    # the first one's transfer cut in 2.  The larger need, 4 slots per head:
     assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 4 * (64 * 128 + 64) * 4
+    assert R.workspace_bytes(4, 4096, 16, 64, 128, 0, 2) == 4 * 16 * 4 * (64 * 128 + 64) * 4
     # long sequence, few heads: segmented
     ws = R.workspace_bytes(1, 65536, 16, 64, 128)
     assert ws > 0 and ws % (16 * (64 * 128 + 64) * 4) == 0
