@@ -108,9 +108,8 @@ template <> struct Pair<__bf16> {
     }
     static __device__ __forceinline__ float lo(type x) { return __uint_as_float(x << 16); }
     static __device__ __forceinline__ float hi(type x) { return __uint_as_float(x & 0xffff0000u); }
-    // run + g * t of the low / high elements: one packed dot product each, with
-    // the other element of t masked to zero (the gates are finite, so the
-    // masked product is an exact zero)
+    // run + g * t of the low / high elements (one packed dot product each; the
+    // operands are the unpacked words, i.e. pairs (0, x))
     static __device__ __forceinline__ float gt_lo(type g, type t, float run) {
         return dot2_bf16(g << 16, t << 16, run);
     }
@@ -876,11 +875,18 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Shapes whose output-mode layout exceeds the CU's LDS (dk = 128 at C = 64)
+// are never planned; they are not instantiated either.
 template <int DK, int DVT, int C, typename TIn>
 hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 {
-    return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true>(Lc, stream)
-                        : launch_mode<DK, DVT, C, TIn, false>(Lc, stream);
+    constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
+    if constexpr (Cfg<DK, DVT, C, NS>::bytes > 160 * 1024) {
+        return hipErrorInvalidValue;
+    } else {
+        return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true>(Lc, stream)
+                            : launch_mode<DK, DVT, C, TIn, false>(Lc, stream);
+    }
 }
 
 // Instantiates every (DVT, C) tile shape for one dk and defines its size
