@@ -16,7 +16,9 @@ once cold, rotating over 12 state batches (1.6 GB).
 
 One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
 per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
-launch / its HIP-event-timed duration), the decode-step bandwidth, the
+launch / its HIP-event-timed duration), the forward on the other workloads
+(``--other-workloads``: the 1.6B-scale layer and the 64K-token prefill, both
+segmented; time per call and algorithmic bandwidth), the decode-step bandwidth, the
 backward (rodimus_ddts_chunk_bwd) on the same batch, a 24K-token prefill
 followed by decode steps from its carried state, and the fp64 CPU oracle
 timed on this host on the same workload (a reported baseline).
@@ -82,6 +84,9 @@ def main():
     ap.add_argument("--serve-batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="layer130m")
+    ap.add_argument("--other-workloads", default="layer1p6b,long_prefill",
+                    help="comma-separated forward workloads timed after the main one "
+                         "('none': skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), "
                          "to scale the HBM byte counters of a profiler run")
@@ -180,6 +185,59 @@ def main():
                          "peak_tflops": BF16_PEAK_TFLOPS,
                          "frac": round(aflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
                          "algorithmic_flops_per_launch": aflops}}
+
+    # ---------------- the other forward workloads (the same timing: settled
+    # clocks, one event pair around back-to-back calls, two rotating input sets)
+    others = {}
+    names = [] if args.other_workloads in ("", "none") else args.other_workloads.split(",")
+    for name in names:
+        if name == args.workload:
+            continue
+        owl = D.WORKLOADS[name]
+        ox = D.make(name)
+        osets = []
+        for r in range(2):
+            t = [ox.torch(n, dev) for n in NAMES]
+            if r:
+                t = [a.clone() for a in t]
+            o_out = torch.empty(owl.B, owl.T, owl.H, owl.dv, device=dev)
+            o_fs = torch.empty(owl.B, owl.H, owl.dk, owl.dv, device=dev) if owl.final_state else None
+            o_s0 = torch.from_numpy(ox.initial_state).to(dev) if ox.initial_state is not None else None
+            osets.append((t, o_s0, o_out, o_fs))
+        owsb = R.workspace_bytes(owl.B, owl.T, owl.H, owl.dk, owl.dv)
+        ows = torch.empty(max(owsb, 1), dtype=torch.uint8, device=dev) if owsb else None
+
+        def ostep(i):
+            t, s0_, out_, fs_ = osets[i % 2]
+            R.chunk_fwd(*t, initial_state=s0_, out=out_, final_state=fs_, workspace=ows)
+
+        i = 0
+        tw = time.perf_counter()
+        while i < 10 or time.perf_counter() - tw < 0.025:
+            ostep(i)
+            i += 1
+            torch.cuda.synchronize()
+        k = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(k):
+            ostep(j)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / k
+        oby, _ = chunk_algorithmic(owl.B, owl.T, owl.H, owl.dk, owl.dv, 64,
+                                   state_in=ox.initial_state is not None, state_out=owl.final_state)
+        others[name] = {"shape": f"B={owl.B} T={owl.T} H={owl.H} dk={owl.dk} dv={owl.dv} bf16 inputs"
+                                 + (", initial state" if ox.initial_state is not None else "")
+                                 + (", returns S_T" if owl.final_state else ""),
+                        "us_per_call": round(us, 2),
+                        "tokens_per_s": round(owl.B * owl.T / (us * 1e-6), 1),
+                        "algorithmic_bytes_per_call": oby,
+                        "algorithmic_GBps": round(oby / us / 1e3, 1),
+                        "frac_hbm": round(oby / us / 1e3 / HBM_PEAK_GBPS, 4),
+                        "workspace_bytes": owsb}
+        del osets, ows
+        torch.cuda.empty_cache()
 
     # ---------------- decode: back-to-back steps over resident states
     decode = None
@@ -324,8 +382,8 @@ def main():
                                    f"bf16 inputs, fp32 out/state, chunk {C}",
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
                        "rotating_input_sets": len(sets), "parallelism": "single GPU"},
-            "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "backward": backward,
-            "serving": serving, "parity": parity}
+            "roofline": roofline, "cpu_baseline": cpu, "other_forward": others or None,
+            "decode": decode, "backward": backward, "serving": serving, "parity": parity}
     print(json.dumps(line), flush=True)
 
 

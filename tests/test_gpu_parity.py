@@ -218,6 +218,14 @@ def test_segmented_transfers_in_four_pieces(R, dev, T, segments):
     check_full(R, x, dev, s0=x.initial_state, segments=segments, label=f"T {T} segments {segments}")
 
 
+@pytest.mark.parametrize("T", [1024, 1000])
+def test_auto_plan_segmented_short_chunks(R, dev, T):
+    # 2 heads x 2 dv tiles fill few CUs, so the planner segments the sequence
+    # and, for bf16 inputs, takes 32-token chunks (4 segments of 8 chunks)
+    x = D.make("long_prefill", B=1, T=T, H=2)
+    check_full(R, x, dev, s0=x.initial_state, label=f"auto plan T {T}")
+
+
 def test_split_sequence_carry_over(R, dev):
     x = D.make("layer1p6b", B=2, T=700, H=3)
     ro, rs = ref(x)
