@@ -87,8 +87,10 @@ size_t rodimus_ddts_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int d
  *   B, T, H, dk, dv  sizes; B, H >= 1, T >= 0 (T == 0 only copies the state).
  *   chunk            tokens per chunk: 0 = library's choice, else 16, 32 or 64.
  *                    Results do not depend on it beyond rounding.  It is an
- *                    upper bound: a shorter chunk is used only where the tile
- *                    does not fit in LDS (fp32 inputs with dk = 128 and 64).
+ *                    upper bound: a shorter chunk is used where the tile does
+ *                    not fit in LDS (fp32 inputs with dk = 128 and 64), and
+ *                    32-token chunks where the library splits the sequences
+ *                    into segments (few (b, h) pairs; bf16 inputs, dk <= 64).
  *   in_dtype         dtype of all six per-token inputs (bf16 or fp32); the
  *                    state and the output are always fp32.
  *   q, k, g, tau     [B, T, H, dk]
