@@ -23,6 +23,7 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_bytes", "bwd_workspace_bytes",
+           "chunk_fwd_plan",
            "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librodimus_ddts.so")
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_chunk_fwd_workspace_bytes.argtypes = [i] * 6
         L.rodimus_ddts_chunk_fwd_ex_workspace_bytes.restype = sz
         L.rodimus_ddts_chunk_fwd_ex_workspace_bytes.argtypes = [i] * 7
+        L.rodimus_ddts_chunk_fwd_plan.restype = i
+        L.rodimus_ddts_chunk_fwd_plan.argtypes = [i] * 8 + [ctypes.POINTER(_ChunkPlan)]
         L.rodimus_ddts_chunk_fwd.restype = i
         L.rodimus_ddts_chunk_fwd.argtypes = [i] * 7 + [vp] * 9 + [vp, sz, vp]
         L.rodimus_ddts_chunk_fwd_ex.restype = i
@@ -122,6 +125,22 @@ def bwd_workspace_bytes(B, T, H, dk, dv) -> int:
 
 def workspace_bytes(B, T, H, dk, dv, chunk=0, segments=0) -> int:
     return int(lib().rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, chunk, segments))
+
+
+class _ChunkPlan(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int), ("dv_tile", ctypes.c_int), ("segments", ctypes.c_int),
+                ("transfer_pieces", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def chunk_fwd_plan(B, T, H, dk, dv, chunk=0, segments=0, dtype="bf16") -> dict:
+    """How the chunk forward runs for these sizes (rodimus_ddts_chunk_fwd_plan):
+    chunk, dv_tile, segments, transfer_pieces, workspace_bytes.  Host only."""
+    code = {"bf16": DTYPE_BF16, "f32": DTYPE_F32}[dtype]
+    p = _ChunkPlan()
+    st = lib().rodimus_ddts_chunk_fwd_plan(B, T, H, dk, dv, chunk, segments, code, ctypes.byref(p))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_chunk_fwd_plan")
+    return {n: int(getattr(p, n)) for n, _ in _ChunkPlan._fields_}
 
 
 def chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None, output_final_state=False,

@@ -25,14 +25,16 @@ Span span(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + by
 
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
-// Pick chunk length, dv tile and segment count.  Returns false if no
-// instantiated tile shape fits the LDS.
+// Pick chunk length, dv tile, segment count and transfer pieces.  Returns
+// false if no instantiated tile shape fits the LDS.
 //  - chunk: the longest of 64/32/16 that is <= the requested one and fits;
-//  - dv tile: 64 columns (4 consumer waves) unless that leaves fewer than
-//    ~160 workgroups and halving it reaches more (then 32);
-//  - segments: when even that leaves fewer than 128 workgroups and the
-//    sequence is long, split it into pieces of >= 8 chunks (64-column tiles,
-//    so the dk-side gate work is shared by as many columns as possible).
+//  - dv tile: min(dv, 64) columns (4 consumer waves at 64, so the dk-side
+//    gate work is shared by as many columns as possible);
+//  - segments (when the caller passes 0): one sweep while the (b, h, tile)
+//    units fill more than half the CUs, else pieces of >= 8 chunks, as many
+//    as run at once, with 32-token chunks where those kernels hold two
+//    workgroups per CU;
+//  - transfer pieces per segment: below.
 bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, bool f32,
                ChunkPlan *P)
 {
@@ -133,6 +135,24 @@ const char *rodimus_status_string(rodimus_status s)
     case RODIMUS_ERR_HIP: return "HIP runtime error";
     }
     return "unknown status";
+}
+
+rodimus_status rodimus_ddts_chunk_fwd_plan(int B, int T, int H, int dk, int dv, int chunk,
+                                           int segments, rodimus_dtype in_dtype,
+                                           rodimus_chunk_plan *plan)
+{
+    if (!plan) return RODIMUS_ERR_INVALID_ARG;
+    rodimus_status st = check_chunk_args(B, T, H, dk, dv, chunk, segments, in_dtype);
+    if (st != RODIMUS_OK) return st;
+    ChunkPlan P;
+    if (!make_plan(B, T, H, dk, dv, chunk, segments, in_dtype == RODIMUS_DTYPE_F32, &P))
+        return RODIMUS_ERR_UNSUPPORTED;
+    plan->chunk = P.C;
+    plan->dv_tile = P.DVT;
+    plan->segments = P.segments;
+    plan->transfer_pieces = P.segments > 1 ? P.tr_per_seg : 0;
+    plan->workspace_bytes = P.ws_bytes;
+    return RODIMUS_OK;
 }
 
 size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,

@@ -135,6 +135,29 @@ size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, in
                                                  int chunk, int segments);
 
 /*
+ * How rodimus_ddts_chunk_fwd_ex runs for these arguments and input dtype:
+ *   chunk            tokens per chunk (16, 32 or 64);
+ *   dv_tile          dv columns per workgroup;
+ *   segments         pieces each (b, h) sequence is split into (1: one
+ *                    sequential sweep);
+ *   transfer_pieces  pieces each state transfer (one per segment but the
+ *                    last) is cut into; 0 for one sweep;
+ *   workspace_bytes  device workspace the call needs (the *_workspace_bytes
+ *                    queries return the larger need over both dtypes).
+ * Host only: no HIP call, no GPU needed; deterministic.  Returns the status
+ * the forward would return for invalid or unsupported arguments (the plan is
+ * then left untouched), RODIMUS_ERR_INVALID_ARG for a NULL plan.
+ */
+typedef struct {
+    int chunk, dv_tile, segments, transfer_pieces;
+    size_t workspace_bytes;
+} rodimus_chunk_plan;
+
+rodimus_status rodimus_ddts_chunk_fwd_plan(int B, int T, int H, int dk, int dv, int chunk,
+                                           int segments, rodimus_dtype in_dtype,
+                                           rodimus_chunk_plan *plan);
+
+/*
  * One recurrent step (sequential inference) for N independent sequences over
  * their resident states, updated in place.
  *

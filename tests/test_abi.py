@@ -217,3 +217,61 @@ def test_bwd_validation():
     assert _bwd(B=0) == R.ERR_INVALID_ARG
     # workspace overlapping an output
     assert _bwd(ws=BASE + 16, wsb=1 << 40) == R.ERR_INVALID_ARG
+
+
+def _plan(*a, **k):
+    return R.chunk_fwd_plan(*a, **k)
+
+
+def test_plan_one_sweep_when_units_fill_the_gpu():
+    # 130M layer: 96 heads x 2 dv tiles of 64 = 192 workgroups: one sweep, 64-token chunks
+    p = _plan(8, 2048, 12, 64, 128)
+    assert p == {"chunk": 64, "dv_tile": 64, "segments": 1, "transfer_pieces": 0,
+                 "workspace_bytes": 0}
+    assert _plan(8, 2048, 12, 64, 128, dtype="f32")["segments"] == 1
+
+
+def test_plan_segmented_bf16_takes_short_chunks():
+    # 1.6B layer: 64 heads x 2 tiles = 128 units, half the CUs.  bf16: 32-token
+    # chunks (two workgroups per CU), 512 / 128 = 4 segments, 3 transfers
+    p = _plan(4, 4096, 16, 64, 128)
+    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (32, 4, 1)
+    assert p["workspace_bytes"] == 4 * 16 * 4 * (64 * 128 + 64) * 4
+    # long prefill: 16 heads x 2 tiles = 32 units -> 16 segments of 128 chunks
+    p = _plan(1, 65536, 16, 64, 128)
+    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (32, 16, 1)
+    # the segment count is capped at one per 8 chunks
+    p = _plan(1, 1024, 2, 64, 128)
+    assert (p["chunk"], p["segments"]) == (32, 4)
+
+
+def test_plan_segmented_fp32_keeps_long_chunks():
+    # fp32 kernels run one workgroup per CU: 64-token chunks, 256 / 128 = 2
+    # segments, the first segment's transfer cut in 2
+    p = _plan(4, 4096, 16, 64, 128, dtype="f32")
+    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (64, 2, 2)
+    assert p["workspace_bytes"] == 4 * 16 * 2 * (64 * 128 + 64) * 4
+
+
+def test_plan_explicit_segments_and_chunk():
+    # an explicit segment count keeps the longest chunk that fits; with 32
+    # chunks per segment the bf16 transfers (two per CU) are cut in 4
+    p = _plan(4, 4096, 16, 64, 128, 0, 2)
+    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (64, 2, 4)
+    # segments = 1 forces one sweep; the chunk request is an upper bound
+    assert _plan(1, 65536, 16, 64, 128, 0, 1)["segments"] == 1
+    assert _plan(8, 2048, 12, 64, 128, 16)["chunk"] == 16
+    # dk = 128: 64-token tiles do not fit the LDS
+    assert _plan(8, 2048, 12, 128, 128)["chunk"] == 32
+    # sequences of fewer than 16 chunks are not split; 16 give 2 segments of 8
+    assert _plan(1, 15 * 32, 1, 64, 128)["segments"] == 1
+    assert _plan(1, 15 * 32 + 1, 1, 64, 128)["segments"] == 2
+
+
+def test_plan_rejects_what_the_forward_rejects():
+    with pytest.raises(R.RodimusError):
+        _plan(1, 100, 1, 48, 128)
+    with pytest.raises(R.RodimusError):
+        _plan(1, 100, 1, 64, 128, 48)
+    with pytest.raises(R.RodimusError):
+        _plan(0, 100, 1, 64, 128)
