@@ -226,6 +226,19 @@ def test_auto_plan_segmented_short_chunks(R, dev, T):
     check_full(R, x, dev, s0=x.initial_state, label=f"auto plan T {T}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 128), (32, 64), (64, 16), (128, 32), (128, 128)])
+def test_auto_plan_segmented_all_widths(R, dev, dk, dv, dtype):
+    # one (b, h) pair over 1100 tokens: the planner segments it (bf16 at
+    # dk <= 64: 32-token chunks, two workgroups per CU; otherwise the longest
+    # chunk that fits); the plan it reports is the one the call runs
+    x = D.make("long_prefill", B=1, T=1100, H=1, dk=dk, dv=dv, dtype=dtype)
+    p = R.chunk_fwd_plan(1, 1100, 1, dk, dv, dtype=dtype)
+    assert p["segments"] > 1
+    assert p["chunk"] == (32 if dtype == "bf16" and dk <= 64 else 64 if dk <= 64 else 32)
+    check_full(R, x, dev, s0=x.initial_state, label=f"auto plan {dk}x{dv} {dtype} {p}")
+
+
 def test_split_sequence_carry_over(R, dev):
     x = D.make("layer1p6b", B=2, T=700, H=3)
     ro, rs = ref(x)
