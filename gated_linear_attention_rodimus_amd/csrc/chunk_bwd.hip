@@ -1117,13 +1117,10 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     constexpr int JT = SweepTile<DK, DV, NS>::JT;     // one workgroup per (b, h, JT columns) and direction
     typedef SweepCfg<DK, JT, NS> SL;
     constexpr size_t sweep_lds = SL::bytes;
-    static bool sweep_attr_set = false;
-    if (!sweep_attr_set) {
-        hipError_t e0 = hipFuncSetAttribute((const void *)state_sweeps_kernel<DK, JT, TIn>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sweep_lds);
-        if (e0 != hipSuccess) return e0;
-        sweep_attr_set = true;
-    }
+    static bool sweep_lds_set[kMaxDevices] = {};
+    hipError_t e0 = set_lds_limit_once((const void *)state_sweeps_kernel<DK, JT, TIn>, sweep_lds,
+                                       sweep_lds_set);
+    if (e0 != hipSuccess) return e0;
     SweepArgs sa;
     sa.T = Lc.T; sa.H = Lc.H; sa.dv = DV; sa.n_chunks = n_chunks;
     sa.q = Lc.in.q; sa.k = Lc.in.k; sa.g = Lc.in.g; sa.tau = Lc.in.tau; sa.v = Lc.in.v; sa.beta = Lc.in.beta;
@@ -1134,13 +1131,9 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    static bool attr_set = false;
-    if (!attr_set) {
-        e = hipFuncSetAttribute((const void *)chunk_grad_kernel<DK, DV, TIn>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool grad_lds_set[kMaxDevices] = {};
+    e = set_lds_limit_once((const void *)chunk_grad_kernel<DK, DV, TIn>, L::bytes, grad_lds_set);
+    if (e != hipSuccess) return e;
     GradArgs ga;
     ga.T = Lc.T; ga.H = Lc.H; ga.n_chunks = n_chunks; ga.n_work = BH * n_chunks;
     ga.q = Lc.in.q; ga.k = Lc.in.k; ga.g = Lc.in.g; ga.tau = Lc.in.tau; ga.v = Lc.in.v;

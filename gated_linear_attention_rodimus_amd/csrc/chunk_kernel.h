@@ -849,13 +849,9 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
     typedef Cfg<DK, DVT, C, NS, OUT> L;
     const size_t lds = L::bytes;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool lds_set[kMaxDevices] = {};
+    hipError_t e = set_lds_limit_once((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT>, lds, lds_set);
+    if (e != hipSuccess) return e;
     Args a;
     a.B = Lc.B; a.T = Lc.T; a.H = Lc.H; a.dv = Lc.dv;
     a.n_seg = Lc.n_seg; a.chunks_per_seg = Lc.chunks_per_seg;

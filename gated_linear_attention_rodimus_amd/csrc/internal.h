@@ -8,6 +8,20 @@
 
 namespace rodimus {
 
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device (the first
+// launch on each device sets it; `done` is that kernel's per-device flags).
+constexpr int kMaxDevices = 64;
+inline hipError_t set_lds_limit_once(const void *fn, size_t bytes, bool *done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && done[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev] = true;
+    return e;
+}
+
 // Per-token input pointers (device), typed as the storage dtype by the kernels.
 struct TokenInputs {
     const void *q, *k, *g, *tau, *v, *beta;
