@@ -116,15 +116,6 @@ template <> struct Pair<__bf16> {
     static __device__ __forceinline__ float gt_hi(type g, type t, float run) {
         return dot2_bf16(g & 0xffff0000u, t & 0xffff0000u, run);
     }
-    // the same sums with one mask per element instead of two unpacks: the
-    // other element of t is zeroed, and g is finite, so that product is an
-    // exact zero.  Fewer VALU instructions, a longer dependency per sum.
-    static __device__ __forceinline__ float gt_lo_m(type g, type t, float run) {
-        return dot2_bf16(g, t & 0x0000ffffu, run);
-    }
-    static __device__ __forceinline__ float gt_hi_m(type g, type t, float run) {
-        return dot2_bf16(g, t & 0xffff0000u, run);
-    }
 };
 template <> struct Pair<float> {
     typedef unsigned type __attribute__((ext_vector_type(2)));
@@ -139,8 +130,6 @@ template <> struct Pair<float> {
     static __device__ __forceinline__ float gt_hi(type g, type t, float run) {
         return __builtin_fmaf(hi(g), hi(t), run);
     }
-    static __device__ __forceinline__ float gt_lo_m(type g, type t, float run) { return gt_lo(g, t, run); }
-    static __device__ __forceinline__ float gt_hi_m(type g, type t, float run) { return gt_hi(g, t, run); }
 };
 
 // Buffer resource over [p, p + bytes); bytes is clamped to 31 bits.  The
@@ -519,17 +508,8 @@ void chunk_fwd_kernel(Args a)
                 float run0 = 0.f, run1 = 0.f;
 #pragma unroll
                 for (int m = 0; m < TPG; ++m) {
-                    // kernels at two workgroups per CU are bound by VALU issue and
-                    // take the masked form (measured ~1-2 % faster on the segmented
-                    // 1.6B layer and long prefill); at one per CU the unpacked form
-                    // measured 2 % faster (130M layer)
-                    if constexpr (L::per_cu == 2) {
-                        run0 = PR::gt_lo_m(rg[R][m], rt[R][m], run0);
-                        run1 = PR::gt_hi_m(rg[R][m], rt[R][m], run1);
-                    } else {
-                        run0 = PR::gt_lo(rg[R][m], rt[R][m], run0);
-                        run1 = PR::gt_hi(rg[R][m], rt[R][m], run1);
-                    }
+                    run0 = PR::gt_lo(rg[R][m], rt[R][m], run0);
+                    run1 = PR::gt_hi(rg[R][m], rt[R][m], run1);
                     cum0[m] = run0;
                     cum1[m] = run1;
                 }
