@@ -235,7 +235,8 @@ def main():
                         "algorithmic_bytes_per_call": oby,
                         "algorithmic_GBps": round(oby / us / 1e3, 1),
                         "frac_hbm": round(oby / us / 1e3 / HBM_PEAK_GBPS, 4),
-                        "workspace_bytes": owsb}
+                        "workspace_bytes": owsb,
+                        "plan": R.chunk_fwd_plan(owl.B, owl.T, owl.H, owl.dk, owl.dv)}
         del osets, ows
         torch.cuda.empty_cache()
 
