@@ -27,8 +27,13 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *    allocates no memory and keeps no state; calls are reentrant.  Work is
- *    enqueued on `stream` and the call returns before it completes.
+ *    allocates no memory and keeps no state beyond a per-device flag for each
+ *    kernel (the first launch of a kernel on a device raises its LDS limit
+ *    with hipFuncSetAttribute); calls are reentrant.  Work is enqueued on
+ *    `stream` and the call returns before it completes.  Only kernel launches
+ *    are enqueued (no memsets, allocations or synchronisation), so calls can
+ *    be captured in a HIP graph; make one call of the same shape and dtype
+ *    outside the capture first, so that the attribute is already set.
  *  - Every argument check happens on the host, synchronously, BEFORE any HIP
  *    call; a failed check returns a status and enqueues nothing.
  *  - Layouts are dense row-major: per-token tensors [B, T, H, D] with the
