@@ -657,8 +657,8 @@ void chunk_grad_kernel(GradArgs a)
     //      then A^T[s][u] = sum_r Kt[s][r] Qt[u][r] by token tiles, over Qt
     constexpr bool kStageGates = !std::is_same<TIn, float>::value;
     const rsrc_t Rgates[4] = {Rq, Rk, Rg, Rt};
+    GateStage<DK, C, NT> gs;                // kept in registers for phase C
     if constexpr (kStageGates) {
-        GateStage<DK, C, NT> gs;
         gs.load(Rgates, HK, tid);
         gs.store((__bf16 *)(smem + L::o_gsa), tid);
         __syncthreads();
@@ -969,10 +969,10 @@ void chunk_grad_kernel(GradArgs a)
 
     // ---- phase C: dA^T into LDS (over dO), then dQt += dA Kt (s <= u) and
     //      dKt += dA^T Qt (u >= s) with Kt and Qt of the dk block as B operands
-    //      (gates read again: bf16 through LDS, the block's Kt and Qt planes
-    //      being free; fp32 directly, from L2)
-    GateStage<DK, C, NT> gsc;
-    if constexpr (kStageGates) gsc.load(Rgates, HK, tid);
+    //      (gates again: bf16 from the words loaded in phase A, still in
+    //      registers, through LDS over the block's Kt and Qt planes, which are
+    //      free by now; fp32 read again directly, from L2)
+    GateStage<DK, C, NT> &gsc = gs;         // the words loaded in phase A
     if (wave < NU) {
         const int st = wave;
 #pragma unroll
