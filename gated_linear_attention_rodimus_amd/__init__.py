@@ -119,6 +119,25 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name}: must be contiguous")
 
 
+def _check_workspace(workspace, need, device):
+    """A caller-supplied workspace: a contiguous tensor on ``device`` holding at
+    least ``need`` bytes (any dtype; its size is numel * element_size).
+    Returns its size in bytes (0 for None).  Raises before any library call."""
+    if workspace is None:
+        return 0
+    torch = _torch()
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError(f"workspace: expected a torch tensor, got {type(workspace).__name__}")
+    if workspace.device != device:
+        raise ValueError(f"workspace: expected device {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace: {nbytes} bytes, the call needs {need}")
+    return nbytes
+
+
 def bwd_workspace_bytes(B, T, H, dk, dv) -> int:
     return int(lib().rodimus_ddts_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
 
@@ -174,11 +193,12 @@ def chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None, output_final_state=
     wsb = workspace_bytes(B, T, H, dk, dv, chunk, segments)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws_bytes = _check_workspace(workspace, wsb, dev)
     st = lib().rodimus_ddts_chunk_fwd_ex(
         B, T, H, dk, dv, int(chunk), int(segments), code,
         _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat),
         _ptr(initial_state), _ptr(out), _ptr(final_state),
-        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(dev))
+        _ptr(workspace), ws_bytes, _stream(dev))
     if st != OK:
         raise RodimusError(st, "rodimus_ddts_chunk_fwd")
     return out, final_state
@@ -241,13 +261,13 @@ def chunk_bwd(q, k, v, g, tau, beta_hat, d_out, initial_state=None, d_final_stat
     wsb = bwd_workspace_bytes(B, T, H, dk, dv)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws_bytes = _check_workspace(workspace, wsb, dev)
     st = lib().rodimus_ddts_chunk_bwd(
         B, T, H, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v),
         _ptr(beta_hat), _ptr(initial_state), _ptr(d_out), _ptr(d_final_state),
         _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dg"]), _ptr(grads["dtau"]),
         _ptr(grads["dv"]), _ptr(grads["dbeta_hat"]), _ptr(grads["d_initial_state"]),
-        _ptr(workspace), ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
-        _stream(dev))
+        _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(dev))
     if st != OK:
         raise RodimusError(st, "rodimus_ddts_chunk_bwd")
     return grads

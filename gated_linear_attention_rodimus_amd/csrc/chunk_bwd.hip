@@ -1117,7 +1117,7 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     constexpr int JT = SweepTile<DK, DV, NS>::JT;     // one workgroup per (b, h, JT columns) and direction
     typedef SweepCfg<DK, JT, NS> SL;
     constexpr size_t sweep_lds = SL::bytes;
-    static bool sweep_lds_set[kMaxDevices] = {};
+    static std::atomic<bool> sweep_lds_set[kMaxDevices];
     hipError_t e0 = set_lds_limit_once((const void *)state_sweeps_kernel<DK, JT, TIn>, sweep_lds,
                                        sweep_lds_set);
     if (e0 != hipSuccess) return e0;
@@ -1131,7 +1131,7 @@ hipError_t launch_typed(const ChunkBwdLaunch &Lc, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    static bool grad_lds_set[kMaxDevices] = {};
+    static std::atomic<bool> grad_lds_set[kMaxDevices];
     e = set_lds_limit_once((const void *)chunk_grad_kernel<DK, DV, TIn>, L::bytes, grad_lds_set);
     if (e != hipSuccess) return e;
     GradArgs ga;

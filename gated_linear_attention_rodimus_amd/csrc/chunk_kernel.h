@@ -849,7 +849,7 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
     typedef Cfg<DK, DVT, C, NS, OUT> L;
     const size_t lds = L::bytes;
-    static bool lds_set[kMaxDevices] = {};
+    static std::atomic<bool> lds_set[kMaxDevices];
     hipError_t e = set_lds_limit_once((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT>, lds, lds_set);
     if (e != hipSuccess) return e;
     Args a;

@@ -2,6 +2,7 @@
 // (host-side launchers; kernels stay private to their .hip file).
 #pragma once
 
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime.h>
@@ -10,15 +11,20 @@ namespace rodimus {
 
 // Raise a kernel's dynamic-LDS limit to `bytes` once per device (the first
 // launch on each device sets it; `done` is that kernel's per-device flags).
+// Host threads may race on a first launch: both then set the same attribute
+// (idempotent) and both store the flag, which is atomic.  Device indices at
+// or beyond kMaxDevices are refused (hipErrorInvalidDevice) rather than
+// setting the attribute on every call.
 constexpr int kMaxDevices = 64;
-inline hipError_t set_lds_limit_once(const void *fn, size_t bytes, bool *done)
+inline hipError_t set_lds_limit_once(const void *fn, size_t bytes, std::atomic<bool> *done)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices && done[dev]) return hipSuccess;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev] = true;
+    if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
     return e;
 }
 

@@ -275,3 +275,41 @@ def test_plan_rejects_what_the_forward_rejects():
         _plan(1, 100, 1, 64, 128, 48)
     with pytest.raises(R.RodimusError):
         _plan(0, 100, 1, 64, 128)
+
+
+def test_named_workspace_query_agrees_with_ex():
+    """rodimus_ddts_chunk_fwd_workspace_bytes is the _ex query with the
+    library's own segment choice (segments = 0), for every chunk request."""
+    L = R.lib()
+    for shape in ((8, 2048, 12, 64, 128), (4, 4096, 16, 64, 128), (1, 65536, 16, 64, 128),
+                  (1, 300, 1, 16, 32), (2, 1000, 3, 128, 64)):
+        for chunk in (0, 16, 32, 64):
+            a = L.rodimus_ddts_chunk_fwd_workspace_bytes(*shape, chunk)
+            b = L.rodimus_ddts_chunk_fwd_ex_workspace_bytes(*shape, chunk, 0)
+            assert a == b, (shape, chunk, a, b)
+    assert L.rodimus_ddts_chunk_fwd_workspace_bytes(1, 65536, 16, 64, 128, 0) > 0
+    assert L.rodimus_ddts_chunk_fwd_workspace_bytes(0, 10, 1, 64, 128, 0) == 0
+
+
+def test_binding_checks_a_supplied_workspace():
+    """A caller's workspace is checked before any library call: its device,
+    contiguity and size in bytes (numel * element_size, any dtype)."""
+    import torch
+    dev = torch.device("cuda:0")
+    assert R._check_workspace(None, 0, dev) == 0
+    cpu = torch.empty(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        R._check_workspace(cpu, 16, dev)
+    meta = torch.empty(1024, dtype=torch.uint8, device="meta")
+    with pytest.raises(ValueError, match="device"):
+        R._check_workspace(meta, 16, dev)
+    with pytest.raises(TypeError):
+        R._check_workspace(bytearray(64), 16, dev)
+    # sizes are counted in bytes: 256 float32 elements hold 1024 bytes
+    f = torch.empty(256, dtype=torch.float32)
+    assert R._check_workspace(f, 1024, torch.device("cpu")) == 1024
+    with pytest.raises(ValueError, match="needs 1025"):
+        R._check_workspace(f, 1025, torch.device("cpu"))
+    nc = torch.empty(64, 4, dtype=torch.uint8).t()
+    with pytest.raises(ValueError, match="contiguous"):
+        R._check_workspace(nc, 16, torch.device("cpu"))
