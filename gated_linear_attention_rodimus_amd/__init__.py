@@ -22,13 +22,14 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_bytes", "bwd_workspace_bytes",
-           "chunk_fwd_plan",
+__all__ = ["chunk_fwd", "chunk_fwd_no_alloc", "chunk_bwd", "decode_step", "workspace_bytes",
+           "bwd_workspace_bytes", "chunk_fwd_plan", "STATIC_SCRATCH_BYTES",
            "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librodimus_ddts.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+STATIC_SCRATCH_BYTES = 32 << 20     # RODIMUS_STATIC_SCRATCH_BYTES
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 _lib = None
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_chunk_fwd.argtypes = [i] * 7 + [vp] * 9 + [vp, sz, vp]
         L.rodimus_ddts_chunk_fwd_ex.restype = i
         L.rodimus_ddts_chunk_fwd_ex.argtypes = [i] * 8 + [vp] * 9 + [vp, sz, vp]
+        L.rodimus_ddts_chunk_fwd_static_scratch.restype = i
+        L.rodimus_ddts_chunk_fwd_static_scratch.argtypes = [i] * 8 + [vp] * 9 + [vp]
         L.rodimus_ddts_decode_step.restype = i
         L.rodimus_ddts_decode_step.argtypes = [i] * 5 + [vp] * 8 + [vp]
         L.rodimus_ddts_chunk_bwd_workspace_bytes.restype = sz
@@ -201,6 +204,37 @@ def chunk_fwd(q, k, v, g, tau, beta_hat, initial_state=None, output_final_state=
         _ptr(workspace), ws_bytes, _stream(dev))
     if st != OK:
         raise RodimusError(st, "rodimus_ddts_chunk_fwd")
+    return out, final_state
+
+
+def chunk_fwd_no_alloc(q, k, v, g, tau, beta_hat, out, initial_state=None, final_state=None,
+                       chunk=0, segments=0):
+    """``chunk_fwd`` for callers that cannot allocate: ``out`` (and
+    ``final_state`` if wanted) are passed in, and the segmented path's scratch
+    is the library's fixed per-GPU buffer (rodimus_ddts_chunk_fwd_static_scratch;
+    at most STATIC_SCRATCH_BYTES of workspace, calls on one GPU must not
+    overlap).  Nothing is allocated here or in the library."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_no_alloc runs on the GPU only; inputs must be on a cuda device")
+    torch = _torch()
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("g", g, dk), ("tau", tau, dk),
+                       ("v", v, dv), ("beta_hat", beta_hat, dv)):
+        _check_tensor(name, t, (B, T, H, d), dt, dev)
+    _check_tensor("out", out, (B, T, H, dv), torch.float32, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _check_tensor(name, t, (B, H, dk, dv), torch.float32, dev)
+    st = lib().rodimus_ddts_chunk_fwd_static_scratch(
+        B, T, H, dk, dv, int(chunk), int(segments), code,
+        _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat),
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_chunk_fwd_static_scratch")
     return out, final_state
 
 

@@ -6,7 +6,17 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 using namespace rodimus;
+
+// Scratch of rodimus_ddts_chunk_fwd_static_scratch: one array per device
+// (each device that loads the library holds its own copy until the process
+// ends).  In host code the name `scratch` is only a host-side stand-in: the
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and kept in scratch_addr, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[RODIMUS_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -176,12 +186,20 @@ size_t rodimus_ddts_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int d
     return rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, chunk, 0);
 }
 
-rodimus_status rodimus_ddts_chunk_fwd_ex(
+}  // extern "C"
+
+namespace {
+
+// Every host-side check of a forward call (sizes, dtype, pointers,
+// alignment, overlaps) and its plan.  With check_ws, also the workspace
+// (size, alignment, overlaps); without, the caller supplies scratch that no
+// tensor can overlap.  No HIP call.
+rodimus_status chunk_fwd_check(
     int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
     const void *q, const void *k, const void *g, const void *tau,
     const void *v, const void *beta_hat,
-    const float *initial_state, float *out, float *final_state,
-    void *workspace, size_t workspace_bytes, hipStream_t stream)
+    const float *initial_state, const float *out, const float *final_state,
+    bool check_ws, const void *workspace, size_t workspace_bytes, ChunkPlan *P)
 {
     rodimus_status st = check_chunk_args(B, T, H, dk, dv, chunk, segments, in_dtype);
     if (st != RODIMUS_OK) return st;
@@ -219,19 +237,28 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
             return RODIMUS_ERR_INVALID_ARG;
     }
 
-    ChunkPlan P;
-    if (!make_plan(B, T, H, dk, dv, chunk, segments, f32, &P)) return RODIMUS_ERR_UNSUPPORTED;
-    if (P.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < P.ws_bytes) return RODIMUS_ERR_WORKSPACE;
+    if (!make_plan(B, T, H, dk, dv, chunk, segments, f32, P)) return RODIMUS_ERR_UNSUPPORTED;
+    if (check_ws && P->ws_bytes > 0) {
+        if (!workspace || workspace_bytes < P->ws_bytes) return RODIMUS_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RODIMUS_ERR_INVALID_ARG;
-        const Span s_ws = span(workspace, P.ws_bytes);
+        const Span s_ws = span(workspace, P->ws_bytes);
         for (const Span &x : s_in)
             if (overlap(s_ws, x)) return RODIMUS_ERR_INVALID_ARG;
         if (overlap(s_ws, s_out) || overlap(s_ws, s_s0) || overlap(s_ws, s_sf))
             return RODIMUS_ERR_INVALID_ARG;
     }
+    return RODIMUS_OK;
+}
 
-    // ---- launches (argument checks are complete)
+// The launches of a checked forward call; `workspace` holds at least
+// P.ws_bytes bytes when P.segments > 1.
+rodimus_status chunk_fwd_launch(
+    const ChunkPlan &P, int B, int T, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, hipStream_t stream)
+{
     hipError_t e = hipSuccess;
     if (T == 0) {
         if (final_state && final_state != initial_state)
@@ -241,7 +268,7 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
     ChunkLaunch Lc;
     Lc.B = B; Lc.T = T; Lc.H = H; Lc.dk = dk; Lc.dv = dv;
     Lc.C = P.C; Lc.DVT = P.DVT; Lc.chunks_per_seg = P.chunks_per_seg;
-    Lc.f32_inputs = f32;
+    Lc.f32_inputs = in_dtype == RODIMUS_DTYPE_F32;
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.gam_out = nullptr;
     Lc.gam_bh_stride = 0;
@@ -280,6 +307,67 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
     Lc.gam_out = nullptr;
     e = launch_chunk(Lc, stream);
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- static scratch
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.
+hipError_t scratch_ptr(void **p)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_addr[dev] = a;
+    }
+    *p = scratch_addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+rodimus_status rodimus_ddts_chunk_fwd_ex(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    ChunkPlan P;
+    rodimus_status st = chunk_fwd_check(B, T, H, dk, dv, chunk, segments, in_dtype, q, k, g, tau,
+                                        v, beta_hat, initial_state, out, final_state, true,
+                                        workspace, workspace_bytes, &P);
+    if (st != RODIMUS_OK) return st;
+    return chunk_fwd_launch(P, B, T, H, dk, dv, in_dtype, q, k, g, tau, v, beta_hat,
+                            initial_state, out, final_state, workspace, stream);
+}
+
+rodimus_status rodimus_ddts_chunk_fwd_static_scratch(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state, hipStream_t stream)
+{
+    ChunkPlan P;
+    rodimus_status st = chunk_fwd_check(B, T, H, dk, dv, chunk, segments, in_dtype, q, k, g, tau,
+                                        v, beta_hat, initial_state, out, final_state, false,
+                                        nullptr, 0, &P);
+    if (st != RODIMUS_OK) return st;
+    if (P.ws_bytes > RODIMUS_STATIC_SCRATCH_BYTES) return RODIMUS_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (T > 0 && P.segments > 1 && scratch_ptr(&ws) != hipSuccess) return RODIMUS_ERR_HIP;
+    return chunk_fwd_launch(P, B, T, H, dk, dv, in_dtype, q, k, g, tau, v, beta_hat,
+                            initial_state, out, final_state, ws, stream);
 }
 
 rodimus_status rodimus_ddts_chunk_fwd(

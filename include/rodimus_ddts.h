@@ -29,7 +29,10 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    allocates no memory and keeps no state beyond a per-device flag for each
  *    kernel (the first launch of a kernel on a device raises its LDS limit
- *    with hipFuncSetAttribute); calls are reentrant.  Work is enqueued on
+ *    with hipFuncSetAttribute) and the fixed per-device scratch array of
+ *    rodimus_ddts_chunk_fwd_static_scratch (part of its code object); calls
+ *    are reentrant, except that calls of that one entry point on one GPU
+ *    share its scratch.  Work is enqueued on
  *    `stream` and the call returns before it completes.  Only kernel launches
  *    are enqueued (no memsets, allocations or synchronisation), so calls can
  *    be captured in a HIP graph; make one call of the same shape and dtype
@@ -138,6 +141,34 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
 
 size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, int dv,
                                                  int chunk, int segments);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as rodimus_ddts_chunk_fwd_ex with identical results, but the scratch
+ * of the segmented path comes from a fixed buffer inside the library instead
+ * of a workspace argument.  The caller still passes inputs and outputs.
+ *
+ *   Limit: the plan's workspace (rodimus_ddts_chunk_fwd_plan) must be at most
+ *   RODIMUS_STATIC_SCRATCH_BYTES, else RODIMUS_ERR_WORKSPACE is returned with
+ *   nothing enqueued (e.g. B * H = 16 heads of 64 x 128 split into 16
+ *   segments need 8.5 MB).
+ *   The buffer is one per GPU, held by every GPU the library runs on until
+ *   the process ends, and shared by every call on that GPU: calls that
+ *   overlap on one GPU (several streams or host threads) race on it and must
+ *   be serialised by the caller.  Its contents carry nothing from one call
+ *   to the next.
+ *   Allocation: none (no hipMalloc, hipFree or allocating library call); the
+ *   first call on a device looks up the buffer's device address once.
+ * Other arguments, checks and errors as rodimus_ddts_chunk_fwd_ex.
+ */
+#define RODIMUS_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+rodimus_status rodimus_ddts_chunk_fwd_static_scratch(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat,
+    const float *initial_state, float *out, float *final_state, hipStream_t stream);
 
 /*
  * How rodimus_ddts_chunk_fwd_ex runs for these arguments and input dtype:

@@ -313,3 +313,30 @@ def test_binding_checks_a_supplied_workspace():
     nc = torch.empty(64, 4, dtype=torch.uint8).t()
     with pytest.raises(ValueError, match="contiguous"):
         R._check_workspace(nc, 16, torch.device("cpu"))
+
+
+def test_static_scratch_entry_rejects_plans_beyond_its_buffer():
+    """The allocation-free forward returns RODIMUS_ERR_WORKSPACE, before any
+    HIP call, when the plan's workspace exceeds the fixed buffer (64 heads in
+    64 segments need ~135 MB), and validates its arguments like the others."""
+    L = R.lib()
+    vp = ctypes.c_void_p
+    B, T, H, dk, dv = 1, 65536, 64, 64, 128
+    need = L.rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, 0, 64)
+    assert need > R.STATIC_SCRATCH_BYTES
+    ntok = B * T * H
+    ptrs, a = [], BASE
+    for d in (dk, dk, dk, dk, dv, dv):
+        ptrs.append(a)
+        a += ((ntok * d * 2 + MB) // 16) * 16
+    out = a
+    st = L.rodimus_ddts_chunk_fwd_static_scratch(B, T, H, dk, dv, 0, 64, R.DTYPE_BF16,
+                                                 *(vp(p) for p in ptrs), None, vp(out), None, None)
+    assert st == R.ERR_WORKSPACE
+    st = L.rodimus_ddts_chunk_fwd_static_scratch(B, T, H, 48, dv, 0, 0, R.DTYPE_BF16,
+                                                 *(vp(p) for p in ptrs), None, vp(out), None, None)
+    assert st == R.ERR_UNSUPPORTED
+    st = L.rodimus_ddts_chunk_fwd_static_scratch(B, T, H, dk, dv, 0, 0, R.DTYPE_BF16,
+                                                 *(vp(p) for p in ptrs), None, vp(ptrs[0]), None,
+                                                 None)
+    assert st == R.ERR_INVALID_ARG            # out overlaps q
