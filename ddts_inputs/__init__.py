@@ -194,3 +194,82 @@ def make_decode_pool(name: str = "decode_batch", pool: int = DECODE_POOL, **over
     sets = [make(name, sub=p + 1, **overrides) for p in range(pool)]
     state = make(name, sub=0, **overrides).initial_state
     return sets, state
+
+
+# tensor ids of the fused-step inputs (their own seed space per workload)
+_QX, _KX, _VX, _UF, _WF, _DF, _CQ, _CK, _CV = range(20, 29)
+
+
+@dataclasses.dataclass
+class FusedInputs:
+    """Inputs of the recurrence with its fused steps.
+
+    ``base`` holds g, tau (and beta_hat, unused when u is given) as in
+    ``make``; q, k, v here carry ``conv_width - 1`` history rows before token
+    0 ([B, T + W - 1, H, D], storage encoding like ``base``).  u [B, T, H, r]
+    and w [H, r, dv] are in the workload's storage encoding; d [H, dv] and the
+    taps conv_q / conv_k [H, dk, W], conv_v [H, dv, W] are float32.
+    """
+    base: Inputs
+    conv_width: int
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    u: np.ndarray
+    w: np.ndarray
+    d: np.ndarray
+    conv_q: np.ndarray
+    conv_k: np.ndarray
+    conv_v: np.ndarray
+
+    def f32(self, name: str) -> np.ndarray:
+        a = getattr(self, name) if name in ("q", "k", "v", "u", "w") else None
+        if a is None:
+            return self.base.f32(name)
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+    def torch(self, name: str, device="cuda"):
+        import torch
+        if name in ("q", "k", "v", "u", "w"):
+            a = getattr(self, name)
+            t = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
+                 else torch.from_numpy(a))
+            return t.to(device)
+        if name in ("d", "conv_q", "conv_k", "conv_v"):
+            return torch.from_numpy(getattr(self, name)).to(device)
+        return self.base.torch(name, device)
+
+
+def make_fused(name: str, conv_width: int = 4, rank: int = 16, sub: int = 0,
+               history: bool = True, **overrides) -> FusedInputs:
+    """A workload's inputs for the fused path: the base draw of ``make``, plus
+    q, k, v with ``conv_width - 1`` history rows (drawn like the tokens, or
+    zeros when ``history`` is False: a sequence start), low-rank factors u,
+    w ~ N(0, 1) (rank ``rank``), d ~ N(0, 1) and ShortConv taps ~ N(0, 1/W)."""
+    base = make(name, sub=sub, **overrides)
+    wl = base.wl
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    W = max(1, conv_width)
+    inv = np.float32(1.0 / math.sqrt(dk))
+
+    def draw(tid, shape, scale=None):
+        x = _rng(wl.wid, tid, sub).standard_normal(shape, dtype=np.float32)
+        if scale is not None:
+            x *= np.float32(scale)
+        return x
+
+    def with_history(tid, d):
+        x = draw(tid, (B, T + W - 1, H, d), inv)
+        if not history:
+            x[:, :W - 1] = 0.0
+        return _encode(x, wl.dtype)
+
+    return FusedInputs(
+        base, W,
+        with_history(_QX, dk), with_history(_KX, dk), with_history(_VX, dv),
+        _encode(draw(_UF, (B, T, H, rank)), wl.dtype),
+        _encode(draw(_WF, (H, rank, dv)), wl.dtype),
+        draw(_DF, (H, dv)),
+        draw(_CQ, (H, dk, W), 1.0 / math.sqrt(W)),
+        draw(_CK, (H, dk, W), 1.0 / math.sqrt(W)),
+        draw(_CV, (H, dv, W), 1.0 / math.sqrt(W)))

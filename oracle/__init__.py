@@ -28,6 +28,14 @@ carry-over; ``bwd`` by ``tests/test_oracle_bwd.py`` against central finite
 differences of ``fwd``, the matmul gradients of the tau = 0 case, dg = 0 at
 tau = 0 and the T = 0 case.
 
+``lowrank_beta``, ``short_conv``, ``fwd_fused`` and ``decode_fused`` are the
+steps the library can fuse around the recurrence (beta_hat from low-rank
+factors, a short causal convolution of q, k and v, the feedthrough d), in
+plain fp64 numpy composed with ``fwd`` / ``decode``; they are pinned by
+``tests/test_oracle_fused.py`` (hand-computed values, an impulse response,
+saturation limits, carry-over of the convolution window and of the state,
+and planted mistakes that the pins must catch).
+
 Inputs may be any numpy floating dtype (bf16 inputs arrive as their exact
 float32 upcast); they are converted to float64 exactly before the C call.
 """
@@ -175,3 +183,80 @@ def rel_to_rms_error(x_hat, x) -> float:
     if rms == 0.0:
         return float(np.max(np.abs(x_hat - x))) if x.size else 0.0
     return float(np.max(np.abs(x_hat - x))) / rms
+
+
+# ---------------------------------------------------------------- fused steps
+# The steps on either side of the recurrence that the library can fuse into
+# its kernels, written out plainly in fp64.  The pages name them without
+# giving their equations, so each follows a stated reading:
+#  - beta_hat from low-rank factors (digest page, "Method", low-rank bullet):
+#    beta_hat_t = sigmoid(u_t W), u_t of rank r per token and head, W [r, dv]
+#    per head, no scaling;
+#  - ShortConv (digest page, "Method", ShortConv + GLU bullet): a causal
+#    depthwise convolution along time of q, k and v, one filter of W taps per
+#    head and channel, no bias, no activation; the W - 1 raw rows before the
+#    first token come with the input (zeros at a sequence start);
+#  - the feedthrough d (rebuttal page, answer to "How significant is d_t in
+#    Eq. (11)?": the SSM feedthrough matrix): o_t += d * v_t, d a per-head
+#    vector over dv constant in t, v_t the value entering the recurrence
+#    (after the convolution, before beta_hat).
+
+
+def lowrank_beta(u, w):
+    """beta_hat = sigmoid(u W) in fp64: u [..., H, r], w [H, r, dv] -> [..., H, dv]."""
+    u = _f64(u)
+    w = _f64(w)
+    z = np.einsum("...hr,hrj->...hj", u, w)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def short_conv(x, c):
+    """Causal depthwise convolution over time in fp64.
+
+    x: [B, T + W - 1, H, D], the W - 1 raw rows before token 0 first;
+    c: [H, D, W], tap j multiplying the input j tokens back.
+    Returns y [B, T, H, D] with y[:, t] = sum_j c[..., j] * x[:, t + W - 1 - j].
+    """
+    x = _f64(x)
+    c = _f64(c)
+    W = c.shape[-1]
+    T = x.shape[1] - (W - 1)
+    assert T >= 0 and c.shape == (x.shape[2], x.shape[3], W)
+    y = np.zeros((x.shape[0], T) + x.shape[2:])
+    for j in range(W):
+        y += c[None, None, :, :, j] * x[:, W - 1 - j:W - 1 - j + T]
+    return y
+
+
+def fwd_fused(q, k, v, g, tau, beta_hat=None, u=None, w=None, d=None, conv=None,
+              initial_state=None, nthreads=0):
+    """The recurrence with its fused steps, in fp64: ShortConv of q, k, v (conv
+    = (c_q, c_k, c_v), each [H, D, W]; q, k, v then carry W - 1 history rows,
+    [B, T + W - 1, H, D]), beta_hat = sigmoid(u w) when u is given (u
+    [B, T, H, r], w [H, r, dv]), then ``fwd``, then o += d * v (d [H, dv]).
+    Returns (o [B, T, H, dv], S_T)."""
+    if conv is not None:
+        cq, ck, cv = conv
+        q, k, v = short_conv(q, cq), short_conv(k, ck), short_conv(v, cv)
+    if u is not None:
+        beta_hat = lowrank_beta(u, w)
+    o, sf = fwd(q, k, v, g, tau, beta_hat, initial_state, nthreads=nthreads)
+    if d is not None:
+        o = o + _f64(d)[None, None] * _f64(v)
+    return o, sf
+
+
+def decode_fused(q, k, v, g, tau, state, beta_hat=None, u=None, w=None, d=None, conv=None):
+    """One recurrent step with the fused steps, in fp64.  Without conv, q, k
+    [N, H, dk] and v [N, H, dv]; with conv, each is the window of its last W
+    raw tokens, oldest first ([N, W, H, D]).  u [N, H, r].  Returns (o [N, H,
+    dv], new state)."""
+    if conv is not None:
+        cq, ck, cv = conv
+        q, k, v = (short_conv(x, c)[:, 0] for x, c in ((q, cq), (k, ck), (v, cv)))
+    if u is not None:
+        beta_hat = lowrank_beta(u, w)
+    o, st = decode(q, k, v, g, tau, beta_hat, state)
+    if d is not None:
+        o = o + _f64(d)[None] * _f64(v)
+    return o, st
