@@ -22,7 +22,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_no_alloc", "chunk_bwd", "decode_step", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_fused", "chunk_fwd_no_alloc", "chunk_bwd", "decode_step",
+           "decode_step_fused", "workspace_bytes", "fused_workspace_bytes",
            "bwd_workspace_bytes", "chunk_fwd_plan", "STATIC_SCRATCH_BYTES",
            "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
@@ -67,6 +68,14 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_chunk_fwd_ex.argtypes = [i] * 8 + [vp] * 9 + [vp, sz, vp]
         L.rodimus_ddts_chunk_fwd_static_scratch.restype = i
         L.rodimus_ddts_chunk_fwd_static_scratch.argtypes = [i] * 8 + [vp] * 9 + [vp]
+        L.rodimus_ddts_chunk_fwd_fused.restype = i
+        L.rodimus_ddts_chunk_fwd_fused.argtypes = ([i] * 8 + [vp] * 6 + [ctypes.POINTER(_Fused)]
+                                                   + [vp] * 4 + [sz, vp])
+        L.rodimus_ddts_chunk_fwd_fused_workspace_bytes.restype = sz
+        L.rodimus_ddts_chunk_fwd_fused_workspace_bytes.argtypes = [i] * 7
+        L.rodimus_ddts_decode_step_fused.restype = i
+        L.rodimus_ddts_decode_step_fused.argtypes = ([i] * 5 + [vp] * 6 + [ctypes.POINTER(_Fused)]
+                                                     + [vp] * 3)
         L.rodimus_ddts_decode_step.restype = i
         L.rodimus_ddts_decode_step.argtypes = [i] * 5 + [vp] * 8 + [vp]
         L.rodimus_ddts_chunk_bwd_workspace_bytes.restype = sz
@@ -147,6 +156,132 @@ def bwd_workspace_bytes(B, T, H, dk, dv) -> int:
 
 def workspace_bytes(B, T, H, dk, dv, chunk=0, segments=0) -> int:
     return int(lib().rodimus_ddts_chunk_fwd_ex_workspace_bytes(B, T, H, dk, dv, chunk, segments))
+
+
+class _Fused(ctypes.Structure):
+    """rodimus_fused: the steps fused around the recurrence."""
+    _fields_ = [("u", ctypes.c_void_p), ("w", ctypes.c_void_p), ("rank", ctypes.c_int),
+                ("d", ctypes.c_void_p), ("conv_width", ctypes.c_int),
+                ("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p),
+                ("conv_v", ctypes.c_void_p)]
+
+
+def fused_workspace_bytes(B, T, H, dk, dv, chunk=0, segments=0) -> int:
+    return int(lib().rodimus_ddts_chunk_fwd_fused_workspace_bytes(B, T, H, dk, dv, chunk, segments))
+
+
+def _fused_desc(u, w, d, conv, H, dk, dv, dt, dev, lead):
+    """Check the fused-step tensors and build the rodimus_fused descriptor.
+    ``lead``: the leading shape of u ((B, T) or (N,))."""
+    torch = _torch()
+    f = _Fused()
+    if u is not None:
+        if w is None:
+            raise ValueError("u needs w")
+        rank = u.shape[-1]
+        _check_tensor("u", u, tuple(lead) + (H, rank), dt, dev)
+        _check_tensor("w", w, (H, rank, dv), dt, dev)
+        f.u, f.w, f.rank = u.data_ptr(), w.data_ptr(), rank
+    if d is not None:
+        _check_tensor("d", d, (H, dv), torch.float32, dev)
+        f.d = d.data_ptr()
+    f.conv_width = 1
+    if conv is not None:
+        cq, ck, cv = conv
+        W = cq.shape[-1]
+        for name, t, n in (("conv_q", cq, dk), ("conv_k", ck, dk), ("conv_v", cv, dv)):
+            _check_tensor(name, t, (H, n, W), torch.float32, dev)
+        f.conv_width = W
+        f.conv_q, f.conv_k, f.conv_v = cq.data_ptr(), ck.data_ptr(), cv.data_ptr()
+    return f
+
+
+def chunk_fwd_fused(q, k, v, g, tau, beta_hat=None, u=None, w=None, d=None, conv=None,
+                    initial_state=None, output_final_state=False, chunk=0, segments=0,
+                    out=None, final_state=None, workspace=None):
+    """Chunk forward with the fused steps (rodimus_ddts_chunk_fwd_fused):
+    beta_hat = sigmoid(u w) when u ([B, T, H, r]) and w ([H, r, dv]) are given
+    (beta_hat then unused), o += d * v when d ([H, dv] fp32) is given, and a
+    ShortConv of q, k, v when conv = (c_q, c_k, c_v) ([H, D, W] fp32) is given,
+    in which case q, k, v are [B, T + W - 1, H, D] with the W - 1 history rows
+    first.  g, tau: [B, T, H, dk].  Returns (o, final state or None)."""
+    torch = _torch()
+    W = 1 if conv is None else conv[0].shape[-1]
+    B, Tx, H, dk = q.shape
+    T = Tx - (W - 1)
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_fused runs on the GPU only; inputs must be on a cuda device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("q", q, (B, Tx, H, dk)), ("k", k, (B, Tx, H, dk)), ("v", v, (B, Tx, H, dv)),
+                         ("g", g, (B, T, H, dk)), ("tau", tau, (B, T, H, dk))):
+        _check_tensor(name, t, shp, dt, dev)
+    if u is None:
+        if beta_hat is None:
+            raise ValueError("beta_hat or (u, w) is needed")
+        _check_tensor("beta_hat", beta_hat, (B, T, H, dv), dt, dev)
+    f = _fused_desc(u, w, d, conv, H, dk, dv, dt, dev, (B, T))
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, (B, T, H, dv), torch.float32, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_tensor("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    wsb = fused_workspace_bytes(B, T, H, dk, dv, chunk, segments)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws_bytes = _check_workspace(workspace, wsb, dev)
+    st = lib().rodimus_ddts_chunk_fwd_fused(
+        B, T, H, dk, dv, int(chunk), int(segments), code,
+        _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat), ctypes.byref(f),
+        _ptr(initial_state), _ptr(out), _ptr(final_state),
+        _ptr(workspace), ws_bytes, _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_chunk_fwd_fused")
+    return out, final_state
+
+
+def decode_step_fused(q, k, v, g, tau, state, beta_hat=None, u=None, w=None, d=None, conv=None,
+                      out=None):
+    """One decode step with the fused steps (rodimus_ddts_decode_step_fused).
+    Without conv, q, k [N, H, dk] and v [N, H, dv]; with conv (W taps), the
+    windows of their last W raw tokens, [N, W, H, D], oldest first.  g, tau
+    [N, H, dk]; u [N, H, r]; state updated in place.  Returns o [N, H, dv]."""
+    torch = _torch()
+    W = 1 if conv is None else conv[0].shape[-1]
+    N, H, dk = g.shape
+    dv = state.shape[-1]
+    dev = g.device
+    if dev.type != "cuda":
+        raise ValueError("decode_step_fused runs on the GPU only; inputs must be on a cuda device")
+    dt = g.dtype
+    code = _dtype_code(g)
+    win = (N, W, H) if conv is not None else (N, H)
+    for name, t, shp in (("q", q, win + (dk,)), ("k", k, win + (dk,)), ("v", v, win + (dv,)),
+                         ("g", g, (N, H, dk)), ("tau", tau, (N, H, dk))):
+        _check_tensor(name, t, shp, dt, dev)
+    if u is None:
+        if beta_hat is None:
+            raise ValueError("beta_hat or (u, w) is needed")
+        _check_tensor("beta_hat", beta_hat, (N, H, dv), dt, dev)
+    f = _fused_desc(u, w, d, conv, H, dk, dv, dt, dev, (N,))
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, (N, H, dv), torch.float32, dev)
+    st = lib().rodimus_ddts_decode_step_fused(
+        N, H, dk, dv, code, _ptr(q), _ptr(k), _ptr(g), _ptr(tau), _ptr(v), _ptr(beta_hat),
+        ctypes.byref(f), _ptr(state), _ptr(out), _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_ddts_decode_step_fused")
+    return out
 
 
 class _ChunkPlan(ctypes.Structure):

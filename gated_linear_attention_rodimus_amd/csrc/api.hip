@@ -46,14 +46,17 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo 
 //    workgroups per CU;
 //  - transfer pieces per segment: below.
 bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, bool f32,
-               ChunkPlan *P)
+               ChunkPlan *P, bool fused = false)
 {
     const int chunks_try[3] = {64, 32, 16};
     bool found = false;
     for (int ci = 0; ci < 3 && !found; ++ci) {
         const int C = chunks_try[ci];
         if (chunk != 0 && C > chunk) continue;
-        const size_t lds = chunk_lds_bytes(dk, dv < 64 ? dv : 64, C, f32);
+        // the fused kernels on fp32 inputs keep a load per ShortConv tap in
+        // registers: 16-token chunks, where they fit without spilling
+        if (fused && f32 && C > 16) continue;
+        const size_t lds = chunk_lds_bytes(dk, dv < 64 ? dv : 64, C, f32, fused);
         if (lds == 0 || lds > kLdsLimit) continue;
         P->C = C;
         found = true;
@@ -74,12 +77,12 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
         // 2 tiles, 4 of C = 32 142 us against 2 of C = 64 151 us)
         if (units <= kTargetBlocks / 2) {
             int Cs = P->C;
-            if (P->C > 32 && chunk_per_cu(dk, dvt, 32, f32, true) == 2 &&
-                chunk_lds_bytes(dk, dvt, 32, f32) != 0)
+            if (P->C > 32 && chunk_per_cu(dk, dvt, 32, f32, true, fused) == 2 &&
+                chunk_lds_bytes(dk, dvt, 32, f32, fused) != 0)
                 Cs = 32;
             const long long nch = T > 0 ? (T + Cs - 1) / Cs : 0;
             if (nch >= 16) {
-                long long want = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, Cs, f32, true) / units;
+                long long want = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, Cs, f32, true, fused) / units;
                 long long cap = nch / 8;
                 seg = (int)(want < cap ? want : cap);
                 if (seg < 1) seg = 1;
@@ -89,7 +92,7 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     }
     P->n_chunks = T > 0 ? (T + P->C - 1) / P->C : 0;
     P->DVT = dvt;
-    P->lds_bytes = chunk_lds_bytes(dk, dvt, P->C, f32);
+    P->lds_bytes = chunk_lds_bytes(dk, dvt, P->C, f32, fused);
     if (P->lds_bytes == 0 || P->lds_bytes > kLdsLimit) return false;
     if (seg > P->n_chunks) seg = P->n_chunks > 0 ? P->n_chunks : 1;
     if (seg < 1) seg = 1;
@@ -103,7 +106,7 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     // heads x 2 tiles x 2 segments of C = 64, 180 -> 153 us), and into 4
     // pieces of at least 8 chunks where the CUs hold that many transfer
     // workgroups
-    const long long xfer_cap = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, P->C, f32, false);
+    const long long xfer_cap = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, P->C, f32, false, fused);
     P->tr_per_seg = 1;
     if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= xfer_cap) P->tr_per_seg = 2;
     if (seg > 1 && P->chunks_per_seg % 4 == 0 && P->chunks_per_seg / 4 >= 8 &&
@@ -194,12 +197,43 @@ namespace {
 // alignment, overlaps) and its plan.  With check_ws, also the workspace
 // (size, alignment, overlaps); without, the caller supplies scratch that no
 // tensor can overlap.  No HIP call.
+// The fused-step descriptor's own checks (sizes, pointers); fills the spans of
+// its tensors.  No HIP call.
+rodimus_status check_fused(const rodimus_fused *f, int B, int T, int H, int dk, int dv,
+                           size_t esz, Span *spans)
+{
+    if (!f) return RODIMUS_ERR_INVALID_ARG;
+    if (f->conv_width < 1 || f->conv_width > 4) return RODIMUS_ERR_UNSUPPORTED;
+    if (f->u && f->rank != 16 && f->rank != 32) return RODIMUS_ERR_UNSUPPORTED;
+    const size_t ntok = (size_t)B * T * H;
+    for (int i = 0; i < 6; ++i) spans[i] = Span{0, 0};
+    if (f->u) {
+        if (!f->w || !aligned16(f->u) || !aligned16(f->w)) return RODIMUS_ERR_INVALID_ARG;
+        spans[0] = span(f->u, ntok * f->rank * esz);
+        spans[1] = span(f->w, (size_t)H * f->rank * dv * esz);
+    }
+    if (f->d) {
+        if (!aligned16(f->d)) return RODIMUS_ERR_INVALID_ARG;
+        spans[2] = span(f->d, (size_t)H * dv * sizeof(float));
+    }
+    if (f->conv_width > 1) {
+        const float *c[3] = {f->conv_q, f->conv_k, f->conv_v};
+        for (const float *p : c)
+            if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+        spans[3] = span(f->conv_q, (size_t)H * dk * f->conv_width * sizeof(float));
+        spans[4] = span(f->conv_k, (size_t)H * dk * f->conv_width * sizeof(float));
+        spans[5] = span(f->conv_v, (size_t)H * dv * f->conv_width * sizeof(float));
+    }
+    return RODIMUS_OK;
+}
+
 rodimus_status chunk_fwd_check(
     int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
     const void *q, const void *k, const void *g, const void *tau,
     const void *v, const void *beta_hat,
     const float *initial_state, const float *out, const float *final_state,
-    bool check_ws, const void *workspace, size_t workspace_bytes, ChunkPlan *P)
+    bool check_ws, const void *workspace, size_t workspace_bytes, ChunkPlan *P,
+    const rodimus_fused *fu = nullptr)
 {
     rodimus_status st = check_chunk_args(B, T, H, dk, dv, chunk, segments, in_dtype);
     if (st != RODIMUS_OK) return st;
@@ -207,20 +241,33 @@ rodimus_status chunk_fwd_check(
     const size_t esz = f32 ? 4 : 2;
     const size_t ntok = (size_t)B * T * H;
     const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+    // q, k, v carry the ShortConv's history rows
+    const int cwid = fu ? fu->conv_width : 1;
+    const size_t ntok_x = (size_t)B * (T + cwid - 1) * H;
+    Span s_fu[6] = {};
+    if (fu) {
+        st = check_fused(fu, B, T, H, dk, dv, esz, s_fu);
+        if (st != RODIMUS_OK) return st;
+    }
+    const bool dense_beta = !fu || !fu->u;
 
     if (T > 0) {
         const void *ins[6] = {q, k, g, tau, v, beta_hat};
-        for (const void *p : ins)
-            if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+        for (int i = 0; i < 6; ++i) {
+            if (i == 5 && !dense_beta) continue;
+            if (!ins[i] || !aligned16(ins[i])) return RODIMUS_ERR_INVALID_ARG;
+        }
         if (!out || !aligned16(out)) return RODIMUS_ERR_INVALID_ARG;
     }
     if (initial_state && !aligned16(initial_state)) return RODIMUS_ERR_INVALID_ARG;
     if (final_state && !aligned16(final_state)) return RODIMUS_ERR_INVALID_ARG;
 
     // aliasing: out may overlap nothing; final_state may equal initial_state
-    const Span s_in[6] = {span(q, ntok * dk * esz), span(k, ntok * dk * esz),
-                          span(g, ntok * dk * esz), span(tau, ntok * dk * esz),
-                          span(v, ntok * dv * esz), span(beta_hat, ntok * dv * esz)};
+    const Span s_in[12] = {span(q, ntok_x * dk * esz), span(k, ntok_x * dk * esz),
+                           span(g, ntok * dk * esz), span(tau, ntok * dk * esz),
+                           span(v, ntok_x * dv * esz),
+                           span(beta_hat, dense_beta ? ntok * dv * esz : 0),
+                           s_fu[0], s_fu[1], s_fu[2], s_fu[3], s_fu[4], s_fu[5]};
     const Span s_out = span(out, ntok * dv * sizeof(float));
     const Span s_s0 = span(initial_state, initial_state ? state_bytes : 0);
     const Span s_sf = span(final_state, final_state ? state_bytes : 0);
@@ -237,7 +284,8 @@ rodimus_status chunk_fwd_check(
             return RODIMUS_ERR_INVALID_ARG;
     }
 
-    if (!make_plan(B, T, H, dk, dv, chunk, segments, f32, P)) return RODIMUS_ERR_UNSUPPORTED;
+    if (!make_plan(B, T, H, dk, dv, chunk, segments, f32, P, fu != nullptr))
+        return RODIMUS_ERR_UNSUPPORTED;
     if (check_ws && P->ws_bytes > 0) {
         if (!workspace || workspace_bytes < P->ws_bytes) return RODIMUS_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RODIMUS_ERR_INVALID_ARG;
@@ -257,7 +305,7 @@ rodimus_status chunk_fwd_launch(
     const void *q, const void *k, const void *g, const void *tau,
     const void *v, const void *beta_hat,
     const float *initial_state, float *out, float *final_state,
-    void *workspace, hipStream_t stream)
+    void *workspace, hipStream_t stream, const rodimus_fused *fu = nullptr)
 {
     hipError_t e = hipSuccess;
     if (T == 0) {
@@ -272,6 +320,12 @@ rodimus_status chunk_fwd_launch(
     Lc.in = TokenInputs{q, k, g, tau, v, beta_hat};
     Lc.gam_out = nullptr;
     Lc.gam_bh_stride = 0;
+    if (fu) {
+        Lc.fused = true;
+        Lc.fu.u = fu->u; Lc.fu.w = fu->w; Lc.fu.rank = fu->rank; Lc.fu.d = fu->d;
+        Lc.fu.conv_w = fu->conv_width;
+        Lc.fu.cq = fu->conv_q; Lc.fu.ck = fu->conv_k; Lc.fu.cv = fu->conv_v;
+    }
     const long long sz = (long long)dk * dv;
     if (P.segments == 1) {
         Lc.n_seg = 1; Lc.mode = 0;
@@ -352,6 +406,37 @@ rodimus_status rodimus_ddts_chunk_fwd_ex(
                             initial_state, out, final_state, workspace, stream);
 }
 
+rodimus_status rodimus_ddts_chunk_fwd_fused(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const rodimus_fused *fused,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    ChunkPlan P;
+    rodimus_status st = chunk_fwd_check(B, T, H, dk, dv, chunk, segments, in_dtype, q, k, g, tau,
+                                        v, beta_hat, initial_state, out, final_state, true,
+                                        workspace, workspace_bytes, &P, fused);
+    if (st != RODIMUS_OK) return st;
+    return chunk_fwd_launch(P, B, T, H, dk, dv, in_dtype, q, k, g, tau, v, beta_hat,
+                            initial_state, out, final_state, workspace, stream, fused);
+}
+
+size_t rodimus_ddts_chunk_fwd_fused_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                                    int chunk, int segments)
+{
+    size_t best = 0;
+    for (int f = 0; f < 2; ++f) {
+        if (check_chunk_args(B, T, H, dk, dv, chunk, segments,
+                             f ? RODIMUS_DTYPE_F32 : RODIMUS_DTYPE_BF16) != RODIMUS_OK)
+            return 0;
+        ChunkPlan P;
+        if (make_plan(B, T, H, dk, dv, chunk, segments, f != 0, &P, true) && P.ws_bytes > best)
+            best = P.ws_bytes;
+    }
+    return best;
+}
+
 rodimus_status rodimus_ddts_chunk_fwd_static_scratch(
     int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
     const void *q, const void *k, const void *g, const void *tau,
@@ -408,6 +493,46 @@ rodimus_status rodimus_ddts_decode_step(
         if (overlap(s_st, x) || overlap(s_o, x)) return RODIMUS_ERR_INVALID_ARG;
     hipError_t e = launch_decode(N, H, dk, dv, in_dtype == RODIMUS_DTYPE_F32,
                                  TokenInputs{q, k, g, tau, v, beta_hat}, state, out, stream);
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+rodimus_status rodimus_ddts_decode_step_fused(
+    int N, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const rodimus_fused *fused,
+    float *state, float *out, hipStream_t stream)
+{
+    if (N <= 0 || H <= 0) return RODIMUS_ERR_INVALID_ARG;
+    if (in_dtype != RODIMUS_DTYPE_F32 && in_dtype != RODIMUS_DTYPE_BF16) return RODIMUS_ERR_UNSUPPORTED;
+    if (!width_ok(dk) || !width_ok(dv)) return RODIMUS_ERR_UNSUPPORTED;
+    if ((long long)N * H > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    const size_t esz = in_dtype == RODIMUS_DTYPE_F32 ? 4 : 2;
+    Span s_fu[6] = {};
+    rodimus_status st = check_fused(fused, N, 1, H, dk, dv, esz, s_fu);
+    if (st != RODIMUS_OK) return st;
+    const bool dense_beta = !fused->u;
+    const void *ins[6] = {q, k, g, tau, v, beta_hat};
+    for (int i = 0; i < 6; ++i) {
+        if (i == 5 && !dense_beta) continue;
+        if (!ins[i] || !aligned16(ins[i])) return RODIMUS_ERR_INVALID_ARG;
+    }
+    if (!state || !out || !aligned16(state) || !aligned16(out)) return RODIMUS_ERR_INVALID_ARG;
+    const size_t pairs = (size_t)N * H, W = (size_t)fused->conv_width;
+    const Span s_st = span(state, pairs * dk * dv * sizeof(float));
+    const Span s_o = span(out, pairs * dv * sizeof(float));
+    const Span s_in[12] = {span(q, W * pairs * dk * esz), span(k, W * pairs * dk * esz),
+                           span(g, pairs * dk * esz), span(tau, pairs * dk * esz),
+                           span(v, W * pairs * dv * esz),
+                           span(beta_hat, dense_beta ? pairs * dv * esz : 0),
+                           s_fu[0], s_fu[1], s_fu[2], s_fu[3], s_fu[4], s_fu[5]};
+    if (overlap(s_st, s_o)) return RODIMUS_ERR_INVALID_ARG;
+    for (const Span &x : s_in)
+        if (overlap(s_st, x) || overlap(s_o, x)) return RODIMUS_ERR_INVALID_ARG;
+    FusedSteps f;
+    f.u = fused->u; f.w = fused->w; f.rank = fused->rank; f.d = fused->d;
+    f.conv_w = fused->conv_width; f.cq = fused->conv_q; f.ck = fused->conv_k; f.cv = fused->conv_v;
+    hipError_t e = launch_decode(N, H, dk, dv, in_dtype == RODIMUS_DTYPE_F32,
+                                 TokenInputs{q, k, g, tau, v, beta_hat}, state, out, stream, &f);
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
 }
 

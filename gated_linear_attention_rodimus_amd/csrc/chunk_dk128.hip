@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK_DK(128)
+RODIMUS_DEFINE_CHUNK(128, false, dk128)
 }  // namespace rodimus

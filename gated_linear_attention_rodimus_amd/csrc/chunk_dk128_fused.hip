@@ -1,0 +1,8 @@
+// chunk_dk128_fused.hip -- chunk-forward kernels for dk = 128 with the fused steps
+// around the recurrence compiled in (beta_hat from low-rank factors, ShortConv
+// of q, k, v, the feedthrough d).  The kernel itself is in chunk_kernel.h.
+#include "chunk_kernel.h"
+
+namespace rodimus {
+RODIMUS_DEFINE_CHUNK(128, true, dk128_fu)
+}  // namespace rodimus

@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK_DK(32)
+RODIMUS_DEFINE_CHUNK(32, false, dk32)
 }  // namespace rodimus

@@ -27,6 +27,18 @@ hipError_t launch_chunk_dk16(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk32(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk64(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk128(const ChunkLaunch &, hipStream_t);
+size_t chunk_lds_bytes_dk16_fu(int, int, bool);
+size_t chunk_lds_bytes_dk32_fu(int, int, bool);
+size_t chunk_lds_bytes_dk64_fu(int, int, bool);
+size_t chunk_lds_bytes_dk128_fu(int, int, bool);
+int chunk_per_cu_dk16_fu(int, int, bool, bool);
+int chunk_per_cu_dk32_fu(int, int, bool, bool);
+int chunk_per_cu_dk64_fu(int, int, bool, bool);
+int chunk_per_cu_dk128_fu(int, int, bool, bool);
+hipError_t launch_chunk_dk16_fu(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk32_fu(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk64_fu(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk128_fu(const ChunkLaunch &, hipStream_t);
 
 namespace {
 
@@ -67,24 +79,24 @@ __global__ __launch_bounds__(256) void state_copy_kernel(const float *__restrict
 
 }  // namespace
 
-size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs)
+size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs, bool fused)
 {
     switch (dk) {
-    case 16: return chunk_lds_bytes_dk16(dvt, C, f32_inputs);
-    case 32: return chunk_lds_bytes_dk32(dvt, C, f32_inputs);
-    case 64: return chunk_lds_bytes_dk64(dvt, C, f32_inputs);
-    case 128: return chunk_lds_bytes_dk128(dvt, C, f32_inputs);
+    case 16: return fused ? chunk_lds_bytes_dk16_fu(dvt, C, f32_inputs) : chunk_lds_bytes_dk16(dvt, C, f32_inputs);
+    case 32: return fused ? chunk_lds_bytes_dk32_fu(dvt, C, f32_inputs) : chunk_lds_bytes_dk32(dvt, C, f32_inputs);
+    case 64: return fused ? chunk_lds_bytes_dk64_fu(dvt, C, f32_inputs) : chunk_lds_bytes_dk64(dvt, C, f32_inputs);
+    case 128: return fused ? chunk_lds_bytes_dk128_fu(dvt, C, f32_inputs) : chunk_lds_bytes_dk128(dvt, C, f32_inputs);
     }
     return 0;
 }
 
-int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs)
+int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs, bool fused)
 {
     switch (dk) {
-    case 16: return chunk_per_cu_dk16(dvt, C, f32_inputs, outputs);
-    case 32: return chunk_per_cu_dk32(dvt, C, f32_inputs, outputs);
-    case 64: return chunk_per_cu_dk64(dvt, C, f32_inputs, outputs);
-    case 128: return chunk_per_cu_dk128(dvt, C, f32_inputs, outputs);
+    case 16: return fused ? chunk_per_cu_dk16_fu(dvt, C, f32_inputs, outputs) : chunk_per_cu_dk16(dvt, C, f32_inputs, outputs);
+    case 32: return fused ? chunk_per_cu_dk32_fu(dvt, C, f32_inputs, outputs) : chunk_per_cu_dk32(dvt, C, f32_inputs, outputs);
+    case 64: return fused ? chunk_per_cu_dk64_fu(dvt, C, f32_inputs, outputs) : chunk_per_cu_dk64(dvt, C, f32_inputs, outputs);
+    case 128: return fused ? chunk_per_cu_dk128_fu(dvt, C, f32_inputs, outputs) : chunk_per_cu_dk128(dvt, C, f32_inputs, outputs);
     }
     return 1;
 }
@@ -92,10 +104,10 @@ int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs)
 hipError_t launch_chunk(const ChunkLaunch &Lc, hipStream_t stream)
 {
     switch (Lc.dk) {
-    case 16: return launch_chunk_dk16(Lc, stream);
-    case 32: return launch_chunk_dk32(Lc, stream);
-    case 64: return launch_chunk_dk64(Lc, stream);
-    case 128: return launch_chunk_dk128(Lc, stream);
+    case 16: return Lc.fused ? launch_chunk_dk16_fu(Lc, stream) : launch_chunk_dk16(Lc, stream);
+    case 32: return Lc.fused ? launch_chunk_dk32_fu(Lc, stream) : launch_chunk_dk32(Lc, stream);
+    case 64: return Lc.fused ? launch_chunk_dk64_fu(Lc, stream) : launch_chunk_dk64(Lc, stream);
+    case 128: return Lc.fused ? launch_chunk_dk128_fu(Lc, stream) : launch_chunk_dk128(Lc, stream);
     }
     return hipErrorInvalidValue;
 }

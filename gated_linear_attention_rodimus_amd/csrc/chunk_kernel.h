@@ -241,6 +241,11 @@ struct Args {
     float *s_out; long long s_out_bh, s_out_seg; int s_out_last_only;
     float *gam_out; long long gam_bh;   // segment decays (mode 1): head bh, segment p at bh * gam_bh + p * DK
     int remap;                   // XCD-aware block mapping on/off
+    // fused steps (kernels instantiated with FU only)
+    const void *u, *w; int rank; // beta_hat = sigmoid(u w) when u is set: u [B][T][H][rank], w [H][rank][dv]
+    const float *dfeed;          // feedthrough o += d * v, d [H][dv], or null
+    int conv_w;                  // ShortConv taps (1: none); q, k, v carry conv_w - 1 history rows
+    const float *cq, *ck, *cv;   // taps [H][D][conv_w]
 };
 
 // v_mul_legacy_f32: an IEEE product, except that 0 times anything (infinities
@@ -267,10 +272,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
 // Compile-time shape of one instantiation, and its LDS layout (bytes).  The
 // segment-transfer mode (OUT_ false) keeps no Qt planes, score tiles or
 // output tile.
-template <int DK, int DVT, int C, int NS_, bool OUT_ = true>
+template <int DK, int DVT, int C, int NS_, bool OUT_ = true, bool FU_ = false>
 struct Cfg {
     static constexpr int NS = NS_;
     static constexpr bool OUT = OUT_;
+    static constexpr bool FU = FU_;                           // fused steps compiled in
+    static constexpr int HALO = FU_ ? 3 : 0;                  // ShortConv history rows (4 taps)
     static constexpr int NP = 4;                              // producer waves
     static constexpr int NJ = DVT / 16;                       // consumer waves
     static constexpr int NW = NP + NJ;
@@ -295,9 +302,12 @@ struct Cfg {
     static constexpr size_t a_off = 2 * buf_bytes;
     static constexpr size_t tot_off = a_off + (OUT ? (size_t)NA * NS * 64 * 4 * 2 : 0);
     static constexpr size_t mid_off = tot_off + (size_t)NG * DK * 4;
-    // per consumer wave: raw v and beta_hat of one chunk, [C][16] bf16 each
+    // per consumer wave: raw v rows of one chunk (with the convolution's
+    // history rows and one row of padding in FU kernels), [SV][16] bf16, then
+    // beta_hat, [C][16]
     static constexpr size_t stg_off = mid_off + (size_t)DK * 4;
-    static constexpr size_t stg_wave = (size_t)2 * C * 16 * 2;
+    static constexpr int SV = C + (FU_ ? HALO + 1 : 0);
+    static constexpr size_t stg_wave = (size_t)(SV + C) * 16 * 2;
     // output tile of one chunk, [C][OS] fp32 (row stride DVT + 16 floats: the
     // four row groups of an MFMA C-layout write land in distinct banks)
     static constexpr int OS = DVT + 16;
@@ -308,19 +318,20 @@ struct Cfg {
     // two fit the CU's LDS and four waves per SIMD leave each wave enough
     // registers (128) without spilling; one otherwise
     static constexpr int per_cu =
-        ((!OUT || C <= 32) && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64) ? 2 : 1;
+        ((!OUT || C <= 32) && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64 && !FU_) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
 
-template <int DK, int DVT, int C, typename TIn, bool OUT>
+template <int DK, int DVT, int C, typename TIn, bool OUT, bool FU>
 __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT),
-                             (Cfg<DK, DVT, C, std::is_same<TIn, float>::value ? 3 : 2, OUT>::waves_per_eu))
+                             (Cfg<DK, DVT, C, std::is_same<TIn, float>::value ? 3 : 2, OUT, FU>::waves_per_eu))
 void chunk_fwd_kernel(Args a)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    typedef Cfg<DK, DVT, C, NS, OUT> L;
+    typedef Cfg<DK, DVT, C, NS, OUT, FU> L;
+    constexpr int HALO = L::HALO;
     typedef typename InRaw<TIn>::type Raw;
     typedef Pair<TIn> PR;
     typedef typename PR::type Raw2;
@@ -367,11 +378,18 @@ void chunk_fwd_kernel(Args a)
     const long long T = a.T, H = a.H, dv = a.dv;
     const long long row_k = H * DK, row_v = H * dv;    // elements between tokens
     const long long head0 = (long long)b * T * H + h;
-    const Raw *gq = (const Raw *)a.q + head0 * DK;
-    const Raw *gk = (const Raw *)a.k + head0 * DK;
+    // q, k, v of FU kernels: [B][T + conv_w - 1][H][D], the convolution's
+    // history rows first; row X of a chunk's window is raw token t0 + X - HALO,
+    // stored at row t0 + X - HALO + conv_w - 1 (rows before 0 read as zero)
+    const int conv_w = FU ? a.conv_w : 1;
+    const long long Tx = T + conv_w - 1;
+    const long long head0x = (long long)b * Tx * H + h;
+    const long long xshift = (long long)conv_w - 1;            // stored row - raw token
+    const Raw *gq = (const Raw *)a.q + head0x * DK;
+    const Raw *gk = (const Raw *)a.k + head0x * DK;
     const Raw *gg = (const Raw *)a.g + head0 * DK;
     const Raw *gt = (const Raw *)a.tau + head0 * DK;
-    const Raw *gv = (const Raw *)a.v + head0 * dv + jcol;
+    const Raw *gv = (const Raw *)a.v + head0x * dv + jcol;
     const Raw *gb = (const Raw *)a.beta + head0 * dv + jcol;
     float *go = a.out ? a.out + head0 * dv + jt * DVT : nullptr;   // this dv tile
 
@@ -475,23 +493,88 @@ void chunk_fwd_kernel(Args a)
         __builtin_amdgcn_s_setprio(2);
         // raw inputs of two chunks (the current one and the next, in flight):
         // a dk column pair, TPG consecutive tokens
-        Raw2 rq[2][TPG], rk[2][TPG], rg[2][TPG], rt[2][TPG];
+        // (FU: q, k with HALO more rows before the group's first token)
+        Raw2 rq[2][TPG + HALO], rk[2][TPG + HALO], rg[2][TPG], rt[2][TPG];
         auto load_dk = [&](int ch, auto rsel, bool valid) {
             constexpr int R = decltype(rsel)::value;
             const long long t0 = (long long)ch * C;
             const long long base = t0 * row_k;
             const long long lim = valid ? ((T - t0) * H - h) * DK * esz : 0;
-            const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
             const __amdgpu_buffer_rsrc_t Rg = make_rsrc(gg + base, lim);
             const __amdgpu_buffer_rsrc_t Rt = make_rsrc(gt + base, lim);
-            const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, lim);
+            if constexpr (FU) {
+                // window rows of the group: raw tokens t0 + cgp*TPG - HALO + i;
+                // the resource starts at the chunk's first stored row, so rows
+                // before the tensor's start have offsets that wrap to beyond its
+                // range and read as zero
+                const long long lx = valid ? ((Tx - t0) * H - h) * DK * esz : 0;
+                const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lx);
+                const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, lx);
 #pragma unroll
-            for (int m = 0; m < TPG; ++m) {
-                const unsigned o = off_k + m * step_k;
-                rg[R][m] = PR::load(Rg, o);
-                rt[R][m] = PR::load(Rt, o);
-                rk[R][m] = PR::load(Rk, o);
-                if (outputs) rq[R][m] = PR::load(Rq, o);
+                for (int i = 0; i < TPG + HALO; ++i) {
+                    const long long row = (long long)cgp * TPG + i - HALO + xshift;
+                    const unsigned o = (unsigned)((row * row_k + c0) * esz);
+                    rk[R][i] = PR::load(Rk, o);
+                    if (outputs) rq[R][i] = PR::load(Rq, o);
+                }
+#pragma unroll
+                for (int m = 0; m < TPG; ++m) {
+                    const unsigned o = off_k + m * step_k;
+                    rg[R][m] = PR::load(Rg, o);
+                    rt[R][m] = PR::load(Rt, o);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t Rk = make_rsrc(gk + base, lim);
+                const __amdgpu_buffer_rsrc_t Rq = make_rsrc(gq + base, lim);
+#pragma unroll
+                for (int m = 0; m < TPG; ++m) {
+                    const unsigned o = off_k + m * step_k;
+                    rg[R][m] = PR::load(Rg, o);
+                    rt[R][m] = PR::load(Rt, o);
+                    rk[R][m] = PR::load(Rk, o);
+                    if (outputs) rq[R][m] = PR::load(Rq, o);
+                }
+            }
+        };
+        // FU: ShortConv taps of this thread's two columns, zero beyond conv_w
+        float tq0[4], tq1[4], tk0[4], tk1[4];
+        if constexpr (FU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool on = prep && j < conv_w && conv_w > 1;
+                const size_t r0 = ((size_t)h * DK + c0) * conv_w + j, r1 = r0 + conv_w;
+                tq0[j] = on && outputs ? a.cq[r0] : 0.f;
+                tq1[j] = on && outputs ? a.cq[r1] : 0.f;
+                tk0[j] = on ? a.ck[r0] : 0.f;
+                tk1[j] = on ? a.ck[r1] : 0.f;
+            }
+        }
+        // q and k of token m of the group (chunk ch, set R): the raw values, or
+        // (FU, conv_w > 1) their convolution over the window, zero past the
+        // sequence end so those tokens stay inert
+        auto qk_at = [&](int ch, auto rsel, int m, float &q0, float &q1, float &k0, float &k1) {
+            constexpr int R = decltype(rsel)::value;
+            if constexpr (FU) {
+                if (conv_w > 1) {
+                    q0 = q1 = k0 = k1 = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = m + HALO - j;
+                        k0 = __builtin_fmaf(tk0[j], PR::lo(rk[R][i]), k0);
+                        k1 = __builtin_fmaf(tk1[j], PR::hi(rk[R][i]), k1);
+                        if (outputs) {
+                            q0 = __builtin_fmaf(tq0[j], PR::lo(rq[R][i]), q0);
+                            q1 = __builtin_fmaf(tq1[j], PR::hi(rq[R][i]), q1);
+                        }
+                    }
+                    if ((long long)ch * C + cgp * TPG + m >= T) q0 = q1 = k0 = k1 = 0.f;
+                } else {
+                    q0 = PR::lo(rq[R][m + HALO]); q1 = PR::hi(rq[R][m + HALO]);
+                    k0 = PR::lo(rk[R][m + HALO]); k1 = PR::hi(rk[R][m + HALO]);
+                }
+            } else {
+                q0 = PR::lo(rq[R][m]); q1 = PR::hi(rq[R][m]);
+                k0 = PR::lo(rk[R][m]); k1 = PR::hi(rk[R][m]);
             }
         };
         float gam_acc0 = 1.f, gam_acc1 = 1.f;           // products of chunk decays (mode 1)
@@ -545,14 +628,16 @@ void chunk_fwd_kernel(Args a)
                     const float d1 = __builtin_fmaf(cum1[m], -kLog2e, sh1);
                     const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
                     const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
+                    float qv0, qv1, kv0, kv1;
+                    qk_at(it, rsel, m, qv0, qv1, kv0, kv1);
                     unsigned pk[NS];
-                    split_pair<NS>(PR::lo(rk[R][m]) * __builtin_amdgcn_exp2f(la0 - d0),
-                                   PR::hi(rk[R][m]) * __builtin_amdgcn_exp2f(la1 - d1), pk);
+                    split_pair<NS>(kv0 * __builtin_amdgcn_exp2f(la0 - d0),
+                                   kv1 * __builtin_amdgcn_exp2f(la1 - d1), pk);
 #pragma unroll
                     for (int n = 0; n < NS; ++n) *(unsigned *)(kb + (n * C + u) * RS + c0) = pk[n];
                     if (outputs) {
-                        split_pair<NS>(PR::lo(rq[R][m]) * __builtin_amdgcn_exp2f(d0),
-                                       PR::hi(rq[R][m]) * __builtin_amdgcn_exp2f(d1), pk);
+                        split_pair<NS>(qv0 * __builtin_amdgcn_exp2f(d0),
+                                       qv1 * __builtin_amdgcn_exp2f(d1), pk);
 #pragma unroll
                         for (int n = 0; n < NS; ++n) *(unsigned *)(qb + (n * C + u) * RS + c0) = pk[n];
                     }
@@ -589,15 +674,102 @@ void chunk_fwd_kernel(Args a)
     // element per load, straight into B-operand order.
     constexpr bool kStage = NS == 2;
     constexpr int LV = C >= 32 ? C / 32 : 1;             // 16-byte loads per tensor
-    u32x4 rvw[LV], rbw[LV];
-    Raw rv[KSC][8], rb[KSC][8];
+    // FU: v window rows X = 0 .. C + HALO - 1 (raw token t0 + X - HALO)
+    constexpr int LVX = FU ? (C + HALO + 31) / 32 : LV;
+    constexpr int NX = FU && !kStage ? 4 : 1;            // fp32 FU: a load per tap
+    u32x4 rvw[LVX], rbw[LV];
+    Raw rv[KSC][8][NX], rb[KSC][8];
     __bf16 *stg = (__bf16 *)(smem + L::stg_off + (size_t)(producer ? 0 : cw) * L::stg_wave);
+    __bf16 *stgb = stg + L::SV * 16;                     // staged beta_hat rows
+    // FU: low-rank beta_hat.  The chunk's u rows as MFMA A operands (16-token
+    // tile T16: lane row lc = token, k = rank index 4 lg.. and 16 + 4 lg..)
+    // and this wave's 16 columns of w as the B operand.
+    const bool lowrank = FU && a.u != nullptr;
+    typedef typename std::conditional<NS == 2, uint2, u32x4>::type URaw;
+    URaw ru[NU][2];
+    bf16x8 wB[NS];
+    if constexpr (FU) {
+        if (lowrank && !producer) {
+            float wv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = (e < 4 ? 0 : 16) + 4 * lg + (e & 3);
+                wv[e] = r < a.rank
+                    ? in_to_f32(((const Raw *)a.w)[((size_t)h * a.rank + r) * a.dv + jcol + lc]) : 0.f;
+            }
+            unsigned w4[4][NS];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_pair<NS>(wv[2 * e], wv[2 * e + 1], w4[e]);
+#pragma unroll
+            for (int n = 0; n < NS; ++n) wB[n] = pack8(w4[0][n], w4[1][n], w4[2][n], w4[3][n]);
+        }
+    }
     auto load_v = [&](int ch, bool valid) {
         const long long t0 = (long long)ch * C;
         const long long base = t0 * row_v;
         const long long lim = valid ? ((T - t0) * H - h) * dv * esz - (long long)jcol * esz : 0;
-        const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lim);
         const __amdgpu_buffer_rsrc_t Rb = make_rsrc(gb + base, lim);
+        if constexpr (FU) {
+            const long long lx = valid ? ((Tx - t0) * H - h) * dv * esz - (long long)jcol * esz : 0;
+            const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lx);
+            if (lowrank) {
+                const long long ru_row = H * (long long)a.rank;
+                const __amdgpu_buffer_rsrc_t Ru = make_rsrc(
+                    (const Raw *)a.u + ((long long)b * T * H + h) * a.rank + t0 * ru_row,
+                    valid ? ((T - t0) * H - h) * (long long)a.rank * esz : 0);
+#pragma unroll
+                for (int t16 = 0; t16 < NU; ++t16)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const unsigned o = (unsigned)(((16 * t16 + lc) * ru_row + 16 * half + 4 * lg) * esz);
+                        if constexpr (NS == 2) {
+                            if (half == 0 || a.rank > 16)
+                                ru[t16][half] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Ru, o, 0, 0));
+                            else
+                                ru[t16][half] = uint2{0u, 0u};
+                        } else {
+                            if (half == 0 || a.rank > 16)
+                                ru[t16][half] = __builtin_amdgcn_raw_buffer_load_b128(Ru, o, 0, 0);
+                            else
+                                ru[t16][half] = u32x4{0u, 0u, 0u, 0u};
+                        }
+                    }
+            }
+            if constexpr (kStage) {
+#pragma unroll
+                for (int j = 0; j < LVX; ++j) {
+                    const int X = (lane >> 1) + 32 * j;
+                    const long long row = (long long)X - HALO + xshift;
+                    const unsigned o = (unsigned)((row * row_v + 8 * (lane & 1)) * esz);
+                    rvw[j] = X < C + HALO ? __builtin_amdgcn_raw_buffer_load_b128(Rv, o, 0, 0)
+                                          : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int j = 0; j < LV; ++j) {
+                    const int u = (lane >> 1) + 32 * j;
+                    const unsigned o = (unsigned)(((long long)u * row_v + 8 * (lane & 1)) * esz);
+                    rbw[j] = u < C && !lowrank ? __builtin_amdgcn_raw_buffer_load_b128(Rb, o, 0, 0)
+                                               : u32x4{0u, 0u, 0u, 0u};
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < KSC; ++p)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int u = p * 32 + (e < 4 ? e : 12 + e) + 4 * lg;
+#pragma unroll
+                        for (int j = 0; j < NX; ++j) {
+                            const long long row = (long long)u - j + xshift;
+                            const unsigned o = (unsigned)((row * row_v + lc) * esz);
+                            rv[p][e][j] = u < C && (j == 0 || conv_w > 1) ? buf_load(Rv, o, Raw()) : Raw(0);
+                        }
+                        const unsigned o = off_v + (p * 32 + (e < 4 ? e : 12 + e)) * step_v;
+                        rb[p][e] = u < C && !lowrank ? buf_load(Rb, o, Raw()) : Raw(0);
+                    }
+            }
+            return;
+        }
+        const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lim);
         if constexpr (kStage) {
 #pragma unroll
             for (int j = 0; j < LV; ++j) {
@@ -619,10 +791,10 @@ void chunk_fwd_kernel(Args a)
                     const int u = p * 32 + (e < 4 ? e : 12 + e);            // + 4*lg via off_v
                     if (u < C) {
                         const unsigned o = off_v + u * step_v;
-                        rv[p][e] = buf_load(Rv, o, Raw());
+                        rv[p][e][0] = buf_load(Rv, o, Raw());
                         rb[p][e] = buf_load(Rb, o, Raw());
                     } else {
-                        rv[p][e] = Raw(0);
+                        rv[p][e][0] = Raw(0);
                         rb[p][e] = Raw(0);
                     }
                 }
@@ -650,6 +822,19 @@ void chunk_fwd_kernel(Args a)
         }
     };
 
+    // FU: ShortConv taps of this lane's v column (zero beyond conv_w), the
+    // feedthrough weight of the column, and the chunk's v values in B-operand
+    // order, kept from phase 1 for the feedthrough in phase 2
+    float tv[4] = {0.f, 0.f, 0.f, 0.f}, dcol = 0.f;
+    float vf[FU ? KSC : 1][8];
+    if constexpr (FU) {
+        if (conv_w > 1)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                tv[j] = j < conv_w ? a.cv[((size_t)h * a.dv + jcol + lc) * conv_w + j] : 0.f;
+        if (a.dfeed) dcol = a.dfeed[(size_t)h * a.dv + jcol + lc];
+    }
+
     for (int it = c_begin; it <= c_end; ++it) {
         const bool cwork = it > c_begin;
         const int cb = (it - 1) & 1;
@@ -676,6 +861,113 @@ void chunk_fwd_kernel(Args a)
         }
         bf16x8 vB[KSC][NS];
         if (cwork) {
+          if constexpr (FU) {
+            // V' = beta_hat * v with the fused steps: v from the convolution
+            // window (or raw), beta_hat from u w (or loaded); both in B-operand
+            // order: element e of a k-step p is token 32 p + 16 (e / 4) + 4 lg
+            // + e % 4 of this lane's column
+            const int tcol = 4 * (lc & 3);
+            const int tok0 = (it - 1) * C;                   // chunk's first token
+            if constexpr (kStage) {
+#pragma unroll
+                for (int j = 0; j < LVX; ++j) {
+                    const int X = (lane >> 1) + 32 * j;
+                    if (X < L::SV) *(u32x4 *)(stg + X * 16 + 8 * (lane & 1)) = rvw[j];
+                }
+                if (!lowrank) {
+#pragma unroll
+                    for (int j = 0; j < LV; ++j) {
+                        const int u = (lane >> 1) + 32 * j;
+                        if (u < C) *(u32x4 *)(stgb + u * 16 + 8 * (lane & 1)) = rbw[j];
+                    }
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < KSC; ++p) {
+                float vv[8], bb[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const bool live = 32 * p + 16 * hh < C;
+                    const int tb = 32 * p + 16 * hh + 4 * lg;    // this lane's first token
+                    if constexpr (kStage) {
+                        const int rr = tb + (lc >> 2);            // row passed by this lane
+                        if (conv_w > 1) {
+                            const bf16x4 x0 = live ? lds_read_tr(stg + rr * 16 + tcol) : zero4();
+                            const bf16x4 x1 = live ? lds_read_tr(stg + (rr + 4) * 16 + tcol) : zero4();
+                            const float xs[8] = {(float)x0[0], (float)x0[1], (float)x0[2], (float)x0[3],
+                                                 (float)x1[0], (float)x1[1], (float)x1[2], (float)x1[3]};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float acc = 0.f;
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(tv[j], xs[e + HALO - j], acc);
+                                vv[4 * hh + e] = acc;
+                            }
+                        } else {
+                            const bf16x4 x0 = live ? lds_read_tr(stg + (rr + HALO) * 16 + tcol) : zero4();
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) vv[4 * hh + e] = (float)x0[e];
+                        }
+                        if (!lowrank) {
+                            const bf16x4 b0 = live ? lds_read_tr(stgb + rr * 16 + tcol) : zero4();
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) bb[4 * hh + e] = (float)b0[e];
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int ee = 4 * hh + e;
+                            float acc = in_to_f32(rv[p][ee][0]);
+                            if (conv_w > 1) {
+                                acc = 0.f;
+#pragma unroll
+                                for (int j = 0; j < NX; ++j) acc = __builtin_fmaf(tv[j], in_to_f32(rv[p][ee][j]), acc);
+                            }
+                            vv[ee] = acc;
+                            bb[ee] = in_to_f32(rb[p][ee]);
+                        }
+                    }
+                    if (lowrank) {
+                        // z = u w for the 16 tokens of tile 2p + hh (C-layout:
+                        // rows 4 lg + e, column lc), then the sigmoid
+                        const int t16 = 2 * p + hh;
+                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        if (live) {
+                            bf16x8 uA[NS];
+                            if constexpr (NS == 2) {
+                                uA[0] = pack8(ru[t16][0].x, ru[t16][0].y, ru[t16][1].x, ru[t16][1].y);
+                                uA[1] = pack8(0u, 0u, 0u, 0u);
+                                z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uA[0], wB[0], z, 0, 0, 0);
+                            } else {
+                                unsigned s4[4][NS];
+                                const u32x4 lo = ru[t16][0], hi2 = ru[t16][1];
+                                split_pair<NS>(__uint_as_float(lo[0]), __uint_as_float(lo[1]), s4[0]);
+                                split_pair<NS>(__uint_as_float(lo[2]), __uint_as_float(lo[3]), s4[1]);
+                                split_pair<NS>(__uint_as_float(hi2[0]), __uint_as_float(hi2[1]), s4[2]);
+                                split_pair<NS>(__uint_as_float(hi2[2]), __uint_as_float(hi2[3]), s4[3]);
+#pragma unroll
+                                for (int n = 0; n < NS; ++n) uA[n] = pack8(s4[0][n], s4[1][n], s4[2][n], s4[3][n]);
+                                z = mma_split<NS>(uA, wB, z);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bb[4 * hh + e] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * z[e]));
+                    }
+                    // tokens past the sequence end stay inert
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (tok0 + tb + e >= T) vv[4 * hh + e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[p][e] = vv[e];
+                unsigned w[4][NS];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) split_pair<NS>(vv[2 * e] * bb[2 * e], vv[2 * e + 1] * bb[2 * e + 1], w[e]);
+#pragma unroll
+                for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
+            }
+          } else {
             // V' = beta_hat * v of this wave's columns, as split B operands (k = tokens)
             if constexpr (kStage) {
                 // stage this wave's rows, then read them back token-major
@@ -710,12 +1002,13 @@ void chunk_fwd_kernel(Args a)
                     unsigned w[4][NS];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e]),
-                                       in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1]), w[e]);
+                        split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e][0]),
+                                       in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1][0]), w[e]);
 #pragma unroll
                     for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
                 }
             }
+          }
             // outputs staged last iteration (issued after the wait for this
             // chunk's v loads, so that wait does not include these stores)
             if (outputs && it - 2 >= c_begin) store_tile(it - 2);
@@ -818,6 +1111,17 @@ void chunk_fwd_kernel(Args a)
                         mma_split_n<NS, NU - 2>(A + 2, Bv + 2, acc + 2);
                     }
                 }
+                // FU: feedthrough o += d * v (C-layout rows 4 lg + r of token
+                // tile U are elements 4 (U & 1) + r of k-step U / 2)
+                if constexpr (FU) {
+                    if (a.dfeed) {
+#pragma unroll
+                        for (int U = 0; U < NU; ++U)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[U][r] = __builtin_fmaf(dcol, vf[U / 2][4 * (U & 1) + r], acc[U][r]);
+                    }
+                }
                 // into the block's output tile; stored to HBM as whole rows
                 // after the next barrier
 #pragma unroll
@@ -843,14 +1147,15 @@ void chunk_fwd_kernel(Args a)
     }
 }
 
-template <int DK, int DVT, int C, typename TIn, bool OUT>
+template <int DK, int DVT, int C, typename TIn, bool OUT, bool FU>
 hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    typedef Cfg<DK, DVT, C, NS, OUT> L;
+    typedef Cfg<DK, DVT, C, NS, OUT, FU> L;
     const size_t lds = L::bytes;
     static std::atomic<bool> lds_set[kMaxDevices];
-    hipError_t e = set_lds_limit_once((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT>, lds, lds_set);
+    hipError_t e = set_lds_limit_once((const void *)chunk_fwd_kernel<DK, DVT, C, TIn, OUT, FU>, lds,
+                                      lds_set);
     if (e != hipSuccess) return e;
     Args a;
     a.B = Lc.B; a.T = Lc.T; a.H = Lc.H; a.dv = Lc.dv;
@@ -864,60 +1169,64 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     a.s_out = Lc.s_out; a.s_out_bh = Lc.s_out_bh_stride; a.s_out_seg = Lc.s_out_seg_stride;
     a.s_out_last_only = Lc.s_out_last_only;
     a.gam_out = Lc.gam_out; a.gam_bh = Lc.gam_bh_stride;
+    a.u = Lc.fu.u; a.w = Lc.fu.w; a.rank = Lc.fu.rank; a.dfeed = Lc.fu.d;
+    a.conv_w = FU ? Lc.fu.conv_w : 1;
+    a.cq = Lc.fu.cq; a.ck = Lc.fu.ck; a.cv = Lc.fu.cv;
     const long long blocks = (long long)Lc.B * Lc.H * Lc.n_seg * a.n_jt;
     a.remap = (blocks % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn, OUT>), dim3((unsigned)blocks), dim3(L::NT),
-                       lds, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_kernel<DK, DVT, C, TIn, OUT, FU>), dim3((unsigned)blocks),
+                       dim3(L::NT), lds, stream, a);
     return hipGetLastError();
 }
 
 // Shapes whose output-mode layout exceeds the CU's LDS (dk = 128 at C = 64)
 // are never planned; they are not instantiated either.
-template <int DK, int DVT, int C, typename TIn>
+template <int DK, int DVT, int C, typename TIn, bool FU>
 hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    if constexpr (Cfg<DK, DVT, C, NS>::bytes > 160 * 1024) {
+    if constexpr (Cfg<DK, DVT, C, NS, true, FU>::bytes > 160 * 1024) {
         return hipErrorInvalidValue;
     } else {
-        return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true>(Lc, stream)
-                            : launch_mode<DK, DVT, C, TIn, false>(Lc, stream);
+        return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true, FU>(Lc, stream)
+                            : launch_mode<DK, DVT, C, TIn, false, FU>(Lc, stream);
     }
 }
 
-// Instantiates every (DVT, C) tile shape for one dk and defines its size
-// query and launcher.
-#define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC)                                            \
+// Instantiates every (DVT, C) tile shape for one dk, with or without the
+// fused steps (XF), and defines its size queries and launcher.
+#define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC, XF)                                        \
     if (dvt == XV && C == XC)                                                         \
-        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3>::bytes : chunk_detail::Cfg<XK, XV, XC, 2>::bytes;
-#define RODIMUS_CHUNK_CASE_PCU(XK, XV, XC)                                            \
+        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true, XF>::bytes                \
+                   : chunk_detail::Cfg<XK, XV, XC, 2, true, XF>::bytes;
+#define RODIMUS_CHUNK_CASE_PCU(XK, XV, XC, XF)                                        \
     if (dvt == XV && C == XC)                                                         \
-        return outputs ? (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true>::per_cu        \
-                              : chunk_detail::Cfg<XK, XV, XC, 2, true>::per_cu)       \
-                       : (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, false>::per_cu       \
-                              : chunk_detail::Cfg<XK, XV, XC, 2, false>::per_cu);
-#define RODIMUS_CHUNK_CASE_LAUNCH(XK, XV, XC)                                         \
+        return outputs ? (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true, XF>::per_cu    \
+                              : chunk_detail::Cfg<XK, XV, XC, 2, true, XF>::per_cu)   \
+                       : (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, false, XF>::per_cu   \
+                              : chunk_detail::Cfg<XK, XV, XC, 2, false, XF>::per_cu);
+#define RODIMUS_CHUNK_CASE_LAUNCH(XK, XV, XC, XF)                                     \
     if (Lc.DVT == XV && Lc.C == XC)                                                   \
-        return Lc.f32_inputs ? chunk_detail::launch_t<XK, XV, XC, float>(Lc, stream)  \
-                             : chunk_detail::launch_t<XK, XV, XC, __bf16>(Lc, stream);
-#define RODIMUS_CHUNK_SHAPES(X, XK)                                                   \
-    X(XK, 16, 16) X(XK, 16, 32) X(XK, 16, 64)                                         \
-    X(XK, 32, 16) X(XK, 32, 32) X(XK, 32, 64)                                         \
-    X(XK, 64, 16) X(XK, 64, 32) X(XK, 64, 64)
-#define RODIMUS_DEFINE_CHUNK_DK(XK)                                                   \
-    size_t chunk_lds_bytes_dk##XK(int dvt, int C, bool f32)                           \
+        return Lc.f32_inputs ? chunk_detail::launch_t<XK, XV, XC, float, XF>(Lc, stream) \
+                             : chunk_detail::launch_t<XK, XV, XC, __bf16, XF>(Lc, stream);
+#define RODIMUS_CHUNK_SHAPES(X, XK, XF)                                               \
+    X(XK, 16, 16, XF) X(XK, 16, 32, XF) X(XK, 16, 64, XF)                             \
+    X(XK, 32, 16, XF) X(XK, 32, 32, XF) X(XK, 32, 64, XF)                             \
+    X(XK, 64, 16, XF) X(XK, 64, 32, XF) X(XK, 64, 64, XF)
+#define RODIMUS_DEFINE_CHUNK(XK, XF, NAME)                                            \
+    size_t chunk_lds_bytes_##NAME(int dvt, int C, bool f32)                           \
     {                                                                                 \
-        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LDS, XK)                              \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LDS, XK, XF)                          \
         return 0;                                                                     \
     }                                                                                 \
-    int chunk_per_cu_dk##XK(int dvt, int C, bool f32, bool outputs)                   \
+    int chunk_per_cu_##NAME(int dvt, int C, bool f32, bool outputs)                   \
     {                                                                                 \
-        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_PCU, XK)                              \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_PCU, XK, XF)                          \
         return 1;                                                                     \
     }                                                                                 \
-    hipError_t launch_chunk_dk##XK(const ChunkLaunch &Lc, hipStream_t stream)         \
+    hipError_t launch_chunk_##NAME(const ChunkLaunch &Lc, hipStream_t stream)         \
     {                                                                                 \
-        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LAUNCH, XK)                           \
+        RODIMUS_CHUNK_SHAPES(RODIMUS_CHUNK_CASE_LAUNCH, XK, XF)                       \
         return hipErrorInvalidValue;                                                  \
     }
 

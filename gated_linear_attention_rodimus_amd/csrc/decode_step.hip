@@ -32,11 +32,33 @@ __device__ __forceinline__ float gate_pow(float g, float tau) {
     return tau == 0.f ? 1.f : 0.f;
 }
 
-template <int DK, int DV, typename TIn>
+// The fused steps of a decode step (FU kernels): beta_hat = sigmoid(u w)
+// when u is set (u [N][H][rank], w [H][rank][dv]), o += d * v when d is set,
+// and a ShortConv of q, k, v over the window of their last conv_w raw tokens
+// ([N][conv_w][H][D], oldest first) when conv_w > 1.
+struct DecodeFused {
+    const void *u, *w;
+    int rank, H, conv_w;
+    const float *d, *cq, *ck, *cv;
+};
+
+template <typename TIn>
+__device__ __forceinline__ float conv_at(const TIn *x, const float *c, int n, int h, int H, int D,
+                                         int i, int W)
+{
+    // y = sum_j c[j] x[newest - j]; window row r holds raw token r (oldest first)
+    float acc = 0.f;
+    for (int j = 0; j < W; ++j)
+        acc = __builtin_fmaf(c[((size_t)h * D + i) * W + j],
+                             ld_in(x, (((size_t)n * W + (W - 1 - j)) * H + h) * D + i), acc);
+    return acc;
+}
+
+template <int DK, int DV, typename TIn, bool FU>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     int pairs, const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ g,
     const TIn *__restrict__ tau, const TIn *__restrict__ v, const TIn *__restrict__ beta,
-    float *__restrict__ state, float *__restrict__ out)
+    float *__restrict__ state, float *__restrict__ out, DecodeFused f)
 {
     constexpr int CG = DV / 4;                       // float4 column groups per row
     constexpr int F4 = DK * DV / 4;                  // float4s per slice
@@ -47,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     static_assert(PER >= 1 && F4 % TPP == 0 && TPP % CG == 0, "tile shape");
 
     __shared__ float s_a[PPB][DK], s_kk[PPB][DK], s_q[PPB][DK], s_vv[PPB][DV];
+    __shared__ float s_vf[FU ? PPB : 1][FU ? DV : 1];    // FU: v entering the recurrence
     __shared__ float s_red[PPB][RG][DV];
 
     const int t = threadIdx.x;
@@ -67,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     }
 
     // gates for this slice (rows over dk, columns over dv)
-    if (active) {
+    if (active && !FU) {
         const size_t rk = (size_t)pair * DK, rv = (size_t)pair * DV;
         for (int i = lt; i < DK; i += TPP) {
             const float gi = ld_in(g, rk + i), ti = ld_in(tau, rk + i);
@@ -77,6 +100,36 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
         }
         for (int j = lt; j < DV; j += TPP)
             s_vv[slot][j] = ld_in(beta, rv + j) * ld_in(v, rv + j);
+    }
+    if constexpr (FU) {
+        if (active) {
+            const int n = pair / f.H, h = pair % f.H;
+            const size_t rk = (size_t)pair * DK, rv = (size_t)pair * DV;
+            for (int i = lt; i < DK; i += TPP) {
+                const float gi = ld_in(g, rk + i), ti = ld_in(tau, rk + i);
+                const float ki = f.conv_w > 1 ? conv_at(k, f.ck, n, h, f.H, DK, i, f.conv_w) : ld_in(k, rk + i);
+                const float qi = f.conv_w > 1 ? conv_at(q, f.cq, n, h, f.H, DK, i, f.conv_w) : ld_in(q, rk + i);
+                s_a[slot][i] = __builtin_amdgcn_exp2f(-gi * ti * kLog2e);
+                s_kk[slot][i] = gate_pow(gi, ti) * ki;
+                s_q[slot][i] = qi;
+            }
+            const TIn *u = (const TIn *)f.u, *w = (const TIn *)f.w;
+            for (int j = lt; j < DV; j += TPP) {
+                const float vj = f.conv_w > 1 ? conv_at(v, f.cv, n, h, f.H, DV, j, f.conv_w) : ld_in(v, rv + j);
+                float bj;
+                if (u) {
+                    float z = 0.f;
+                    for (int r = 0; r < f.rank; ++r)
+                        z = __builtin_fmaf(ld_in(u, (size_t)pair * f.rank + r),
+                                           ld_in(w, ((size_t)h * f.rank + r) * DV + j), z);
+                    bj = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * z));
+                } else {
+                    bj = ld_in(beta, rv + j);
+                }
+                s_vv[slot][j] = bj * vj;
+                s_vf[slot][j] = vj;
+            }
+        }
     }
     __syncthreads();
 
@@ -109,6 +162,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < RG; ++r) acc += s_red[slot][r][j];
+            if constexpr (FU) {
+                if (f.d) acc = __builtin_fmaf(f.d[(size_t)(pair % f.H) * DV + j], s_vf[slot][j], acc);
+            }
             out[(size_t)pair * DV + j] = acc;
         }
     }
@@ -116,27 +172,35 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 
 template <int DK, int DV, typename TIn>
 hipError_t launch_typed(int pairs, const TokenInputs &in, float *state, float *out,
-                        hipStream_t stream)
+                        const DecodeFused *f, hipStream_t stream)
 {
     constexpr int F4 = DK * DV / 4;
     constexpr int PPB = F4 >= kThreads ? 1 : kThreads / F4;
     const int blocks = (pairs + PPB - 1) / PPB;
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn>), dim3(blocks), dim3(kThreads), 0, stream,
-                       pairs, (const TIn *)in.q, (const TIn *)in.k, (const TIn *)in.g,
-                       (const TIn *)in.tau, (const TIn *)in.v, (const TIn *)in.beta, state, out);
+    if (f) {
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn, true>), dim3(blocks), dim3(kThreads), 0,
+                           stream, pairs, (const TIn *)in.q, (const TIn *)in.k, (const TIn *)in.g,
+                           (const TIn *)in.tau, (const TIn *)in.v, (const TIn *)in.beta, state, out,
+                           *f);
+    } else {
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn, false>), dim3(blocks), dim3(kThreads), 0,
+                           stream, pairs, (const TIn *)in.q, (const TIn *)in.k, (const TIn *)in.g,
+                           (const TIn *)in.tau, (const TIn *)in.v, (const TIn *)in.beta, state, out,
+                           DecodeFused{});
+    }
     return hipGetLastError();
 }
 
 template <typename TIn>
 hipError_t launch_dtype(int pairs, int dk, int dv, const TokenInputs &in, float *state,
-                        float *out, hipStream_t stream)
+                        float *out, const DecodeFused *f, hipStream_t stream)
 {
 #define RODIMUS_DEC_DV(DK)                                                              \
     switch (dv) {                                                                       \
-    case 16: return launch_typed<DK, 16, TIn>(pairs, in, state, out, stream);           \
-    case 32: return launch_typed<DK, 32, TIn>(pairs, in, state, out, stream);           \
-    case 64: return launch_typed<DK, 64, TIn>(pairs, in, state, out, stream);           \
-    case 128: return launch_typed<DK, 128, TIn>(pairs, in, state, out, stream);         \
+    case 16: return launch_typed<DK, 16, TIn>(pairs, in, state, out, f, stream);        \
+    case 32: return launch_typed<DK, 32, TIn>(pairs, in, state, out, f, stream);        \
+    case 64: return launch_typed<DK, 64, TIn>(pairs, in, state, out, f, stream);        \
+    case 128: return launch_typed<DK, 128, TIn>(pairs, in, state, out, f, stream);      \
     }                                                                                   \
     break;
     switch (dk) {
@@ -152,11 +216,18 @@ hipError_t launch_dtype(int pairs, int dk, int dv, const TokenInputs &in, float 
 }  // namespace
 
 hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
-                         float *state, float *out, hipStream_t stream)
+                         float *state, float *out, hipStream_t stream, const FusedSteps *fused)
 {
     const int pairs = N * H;
-    return f32_inputs ? launch_dtype<float>(pairs, dk, dv, in, state, out, stream)
-                      : launch_dtype<__bf16>(pairs, dk, dv, in, state, out, stream);
+    DecodeFused f{};
+    if (fused) {
+        f.u = fused->u; f.w = fused->w; f.rank = fused->rank; f.H = H;
+        f.conv_w = fused->conv_w; f.d = fused->d;
+        f.cq = fused->cq; f.ck = fused->ck; f.cv = fused->cv;
+    }
+    const DecodeFused *fp = fused ? &f : nullptr;
+    return f32_inputs ? launch_dtype<float>(pairs, dk, dv, in, state, out, fp, stream)
+                      : launch_dtype<__bf16>(pairs, dk, dv, in, state, out, fp, stream);
 }
 
 }  // namespace rodimus

@@ -48,11 +48,25 @@ struct ChunkPlan {
     size_t ws_bytes;
 };
 
-// Bytes of LDS the chunk kernel needs for a tile shape (0 if not instantiated).
-size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs);
+// Bytes of LDS the chunk kernel needs for a tile shape (0 if not instantiated),
+// with or without the fused steps.
+size_t chunk_lds_bytes(int dk, int dvt, int C, bool f32_inputs, bool fused = false);
 // Workgroups of the output mode (outputs true) or of the segment-transfer
 // mode one CU holds for a tile shape.
-int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs);
+int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs, bool fused = false);
+
+// The steps fused around the recurrence (kernels instantiated with them):
+// beta_hat = sigmoid(u w) when u is set (u [B][T][H][rank], w [H][rank][dv],
+// the inputs' dtype), the feedthrough o += d * v (d [H][dv] fp32, or null),
+// and a ShortConv of q, k, v with conv_w taps (1: none; c* [H][D][conv_w]
+// fp32; q, k, v then hold conv_w - 1 history rows before token 0).
+struct FusedSteps {
+    const void *u = nullptr, *w = nullptr;
+    int rank = 0;
+    const float *d = nullptr;
+    int conv_w = 1;
+    const float *cq = nullptr, *ck = nullptr, *cv = nullptr;
+};
 
 // Chunk sweep / segment pass.  mode 0: outputs from S_in; mode 1: segment
 // state transfer (dS from a zero state, and the product of decays).
@@ -67,6 +81,8 @@ struct ChunkLaunch {
     float *s_out; long long s_out_bh_stride, s_out_seg_stride; int s_out_last_only;
     float *gam_out;         // mode 1: segment p's decay of head bh at bh * gam_bh_stride + p * dk
     long long gam_bh_stride;
+    bool fused = false;     // run the kernels with the fused steps compiled in
+    FusedSteps fu;
 };
 hipError_t launch_chunk(const ChunkLaunch &L, hipStream_t stream);
 
@@ -81,7 +97,8 @@ hipError_t launch_segment_combine(int BH, int n_seg, int per, int slots, int dk,
 hipError_t launch_state_copy(const float *src, float *dst, size_t count, hipStream_t stream);
 
 hipError_t launch_decode(int N, int H, int dk, int dv, bool f32_inputs, const TokenInputs &in,
-                         float *state, float *out, hipStream_t stream);
+                         float *state, float *out, hipStream_t stream,
+                         const FusedSteps *fused = nullptr);
 
 // Backward of the chunk forward: one launch runs the forward state sweep
 // (the state entering every chunk, and S_T) and the reverse adjoint sweep

@@ -194,6 +194,58 @@ rodimus_status rodimus_ddts_chunk_fwd_plan(int B, int T, int H, int dk, int dv, 
                                            rodimus_chunk_plan *plan);
 
 /*
+ * The steps on either side of the recurrence, fused into its kernels.  The
+ * pages name them without giving their equations; the readings taken:
+ *  - beta_hat from low-rank factors (digest page, "Method", low-rank
+ *    bullet): beta_hat_t = sigmoid(u_t w), u_t the rank-r factor of token t
+ *    and head h, w [r, dv] per head, no scaling;
+ *  - ShortConv (digest page, "Method", ShortConv + GLU bullet): a causal
+ *    depthwise convolution along time of q, k and v, conv_width taps per head
+ *    and channel, no bias, no activation:
+ *        x'_t[i] = sum_{j < conv_width} c[h][i][j] x_{t-j}[i];
+ *  - the feedthrough d (rebuttal page, answer to "How significant is d_t in
+ *    Eq. (11)?": the SSM feedthrough matrix): o_t += d .* v_t, d a vector over
+ *    dv per head, constant in t, v_t the value entering the recurrence (after
+ *    the convolution, before beta_hat).
+ * Fields (NULL / 0 / 1 switch a step off):
+ *   u, w        [B, T, H, rank] (decode: [N, H, rank]) and [H, rank, dv], in
+ *               in_dtype; rank 16 or 32.  When u is set, beta_hat is not read
+ *               and may be NULL.
+ *   d           [H, dv] fp32.
+ *   conv_width  1 (none), 2, 3 or 4; conv_q, conv_k [H, dk, conv_width] and
+ *               conv_v [H, dv, conv_width] fp32, tap j multiplying the input
+ *               j tokens back.  q, k and v then hold conv_width - 1 raw rows
+ *               before token 0: [B, T + conv_width - 1, H, D] (zeros at a
+ *               sequence start; the last conv_width - 1 raw rows of the
+ *               previous call to continue a sequence).  Decode: q, k, v are the
+ *               windows of the last conv_width raw tokens, oldest first,
+ *               [N, conv_width, H, D].
+ * All pointers 16-byte aligned, outputs overlapping none of them.
+ */
+typedef struct {
+    const void *u, *w;
+    int rank;
+    const float *d;
+    int conv_width;
+    const float *conv_q, *conv_k, *conv_v;
+} rodimus_fused;
+
+/*
+ * rodimus_ddts_chunk_fwd_ex with the fused steps of `fused` (not NULL).
+ * Workspace: rodimus_ddts_chunk_fwd_fused_workspace_bytes (the fused kernels
+ * may plan differently: fp32 inputs run 16-token chunks).
+ */
+rodimus_status rodimus_ddts_chunk_fwd_fused(
+    int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const rodimus_fused *fused,
+    const float *initial_state, float *out, float *final_state,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t rodimus_ddts_chunk_fwd_fused_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                                    int chunk, int segments);
+
+/*
  * One recurrent step (sequential inference) for N independent sequences over
  * their resident states, updated in place.
  *
@@ -209,6 +261,16 @@ rodimus_status rodimus_ddts_decode_step(
     int N, int H, int dk, int dv, rodimus_dtype in_dtype,
     const void *q, const void *k, const void *g, const void *tau,
     const void *v, const void *beta_hat,
+    float *state, float *out, hipStream_t stream);
+
+/*
+ * rodimus_ddts_decode_step with the fused steps of `fused` (not NULL); q, k,
+ * v are [N, conv_width, H, D] windows when conv_width > 1.
+ */
+rodimus_status rodimus_ddts_decode_step_fused(
+    int N, int H, int dk, int dv, rodimus_dtype in_dtype,
+    const void *q, const void *k, const void *g, const void *tau,
+    const void *v, const void *beta_hat, const rodimus_fused *fused,
     float *state, float *out, hipStream_t stream);
 
 /*

@@ -1,0 +1,242 @@
+"""GPU parity of the fused steps around the recurrence (beta_hat from low-rank
+factors, ShortConv of q, k, v, the feedthrough d) through the C ABI, against
+the fp64 oracle's fwd_fused / decode_fused on the same bf16-rounded (or fp32)
+values.  Bars as everywhere: max |x_hat - x| / RMS(x) <= 1e-2 for bf16
+inputs, 1e-4 for fp32, outputs and states separately."""
+import numpy as np
+import pytest
+
+import ddts_inputs as D
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+BAR = {"bf16": 1e-2, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def R():
+    import gated_linear_attention_rodimus_amd as mod
+    mod.lib()
+    return mod
+
+
+DEV = None
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def run(R, f, use_u=True, use_d=True, use_conv=True, s0=None, final=True, chunk=0, segments=0):
+    t = {n: f.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "beta_hat", "u", "w", "d",
+                                         "conv_q", "conv_k", "conv_v")}
+    s0d = None if s0 is None else torch.from_numpy(np.ascontiguousarray(s0, np.float32)).to(dev())
+    q, k, v = t["q"], t["k"], t["v"]
+    W = f.conv_width
+    if not use_conv:                       # drop the history rows: plain q, k, v
+        q, k, v = (x[:, W - 1:].contiguous() for x in (q, k, v))
+    o, sf = R.chunk_fwd_fused(q, k, v, t["g"], t["tau"],
+                              beta_hat=None if use_u else t["beta_hat"],
+                              u=t["u"] if use_u else None, w=t["w"] if use_u else None,
+                              d=t["d"] if use_d else None,
+                              conv=(t["conv_q"], t["conv_k"], t["conv_v"]) if use_conv else None,
+                              initial_state=s0d, output_final_state=final, chunk=chunk,
+                              segments=segments)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), (None if sf is None else sf.cpu().numpy())
+
+
+def ref(f, use_u=True, use_d=True, use_conv=True, s0=None):
+    W = f.conv_width
+    q, k, v = f.f32("q"), f.f32("k"), f.f32("v")
+    if not use_conv:
+        q, k, v = q[:, W - 1:], k[:, W - 1:], v[:, W - 1:]
+    return oracle.fwd_fused(q, k, v, f.f32("g"), f.f32("tau"),
+                            beta_hat=None if use_u else f.f32("beta_hat"),
+                            u=f.f32("u") if use_u else None, w=f.f32("w") if use_u else None,
+                            d=f.d if use_d else None,
+                            conv=(f.conv_q, f.conv_k, f.conv_v) if use_conv else None,
+                            initial_state=s0)
+
+
+def check(R, f, label, **kw):
+    s0 = kw.pop("s0", None)
+    chunk = kw.pop("chunk", 0)
+    segments = kw.pop("segments", 0)
+    o, sf = run(R, f, s0=s0, chunk=chunk, segments=segments, **kw)
+    ro, rs = ref(f, s0=s0, **kw)
+    bar = BAR[f.base.wl.dtype]
+    eo, es = oracle.rel_to_rms_error(o, ro), oracle.rel_to_rms_error(sf, rs)
+    print(f"[{label}] out err {eo:.2e} state err {es:.2e} bar {bar:g}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(sf).all()
+    assert eo <= bar and es <= bar
+    return o, sf
+
+
+def test_layer130m_full_with_lowrank_beta(R):
+    """The 130M layer (B8 T2048 H12) fed its rank-16 factors u, w instead of
+    a dense beta_hat: 224 fewer bytes per token and head."""
+    f = D.make_fused("layer130m", conv_width=1)
+    check(R, f, "layer130m u,w rank16", use_d=False, use_conv=False)
+
+
+@pytest.mark.parametrize("rank", [16, 32])
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_all_steps_ragged(R, rank, W):
+    f = D.make_fused("layer130m", conv_width=W, rank=rank, B=2, T=333, H=3)
+    rng = np.random.default_rng(W * 100 + rank)
+    s0 = (0.1 * rng.standard_normal((2, 3, 64, 128))).astype(np.float32)
+    check(R, f, f"all steps W{W} rank{rank} B2 T333 H3", s0=s0)
+
+
+@pytest.mark.parametrize("which", ["u", "d", "conv"])
+def test_each_step_alone(R, which):
+    f = D.make_fused("layer130m", conv_width=4, B=1, T=200, H=4)
+    check(R, f, f"only {which}", use_u=which == "u", use_d=which == "d", use_conv=which == "conv")
+
+
+def test_no_history_is_a_sequence_start(R):
+    f = D.make_fused("layer130m", conv_width=4, B=2, T=97, H=2, history=False)
+    check(R, f, "zero history")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 128), (64, 32)])
+def test_widths(R, dk, dv):
+    f = D.make_fused("layer130m", conv_width=3, B=1, T=150, H=2, dk=dk, dv=dv)
+    check(R, f, f"widths dk{dk} dv{dv}")
+
+
+def test_segmented_long_prefill_slice(R):
+    """The long prefill's shape class (few heads, long sequence, initial
+    state): the segmented plan, with every fused step in both passes."""
+    f = D.make_fused("long_prefill", conv_width=4, T=8192 + 5, H=4)
+    p = R.fused_workspace_bytes(1, 8192 + 5, 4, 64, 128)
+    assert p > 0
+    check(R, f, "segmented long prefill slice", s0=f.base.initial_state)
+
+
+def test_explicit_segments_and_chunks(R):
+    f = D.make_fused("layer130m", conv_width=4, B=1, T=700, H=2)
+    for chunk, seg in ((16, 3), (32, 5), (64, 2), (32, 1)):
+        check(R, f, f"chunk {chunk} segments {seg}", chunk=chunk, segments=seg)
+
+
+def test_fp32_inputs(R):
+    f = D.make_fused("tiny", conv_width=4, T=77, H=2, dk=32, dv=16)
+    rng = np.random.default_rng(1)
+    s0 = (0.1 * rng.standard_normal((1, 2, 32, 16))).astype(np.float32)
+    check(R, f, "fp32 all steps", s0=s0)
+
+
+def test_all_steps_off_matches_plain_forward(R):
+    """With no step switched on the fused kernels reproduce the plain forward
+    bit for bit (same plan on this one-sweep shape)."""
+    x = D.make("layer130m", B=2, T=300, H=12)
+    t = [x.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "beta_hat")]
+    o1, s1 = R.chunk_fwd(*t, output_final_state=True)
+    o2, s2 = R.chunk_fwd_fused(*t, output_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_split_sequence_carry_over(R):
+    """Two calls over halves, the second fed the last W - 1 raw rows of the
+    first as its history and the first's final state, equal one call."""
+    W, T1, T2 = 4, 160, 141
+    f = D.make_fused("layer130m", conv_width=W, B=2, T=T1 + T2, H=3)
+    t = {n: f.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "u", "w", "d",
+                                         "conv_q", "conv_k", "conv_v")}
+    conv = (t["conv_q"], t["conv_k"], t["conv_v"])
+    kw = dict(u=None, w=t["w"], d=t["d"], conv=conv)
+    o, sf = R.chunk_fwd_fused(t["q"], t["k"], t["v"], t["g"], t["tau"], u=t["u"], w=t["w"],
+                              d=t["d"], conv=conv, output_final_state=True)
+    cut = lambda x, a, b: x[:, a:b].contiguous()
+    o1, s1 = R.chunk_fwd_fused(cut(t["q"], 0, W - 1 + T1), cut(t["k"], 0, W - 1 + T1),
+                               cut(t["v"], 0, W - 1 + T1), cut(t["g"], 0, T1), cut(t["tau"], 0, T1),
+                               u=cut(t["u"], 0, T1), w=t["w"], d=t["d"], conv=conv,
+                               output_final_state=True)
+    o2, s2 = R.chunk_fwd_fused(cut(t["q"], T1, W - 1 + T1 + T2), cut(t["k"], T1, W - 1 + T1 + T2),
+                               cut(t["v"], T1, W - 1 + T1 + T2), cut(t["g"], T1, T1 + T2),
+                               cut(t["tau"], T1, T1 + T2), u=cut(t["u"], T1, T1 + T2), w=t["w"],
+                               d=t["d"], conv=conv, initial_state=s1, output_final_state=True)
+    torch.cuda.synchronize()
+    whole = o.cpu().numpy()
+    parts = np.concatenate([o1.cpu().numpy(), o2.cpu().numpy()], axis=1)
+    e = oracle.rel_to_rms_error(parts, whole)
+    es = oracle.rel_to_rms_error(s2.cpu().numpy(), sf.cpu().numpy())
+    print(f"[split carry] out {e:.2e} state {es:.2e}", flush=True)
+    assert e <= 1e-3 and es <= 1e-3
+
+
+# ---------------------------------------------------------------- decode
+
+
+def test_decode_fused_steps(R):
+    """Decode steps with rolling convolution windows, low-rank beta_hat and
+    the feedthrough, from a prefill's carried state, against the oracle's
+    fused forward over the whole sequence."""
+    W, Tp, Td = 4, 96, 12
+    f = D.make_fused("decode_batch", conv_width=W, B=8, T=Tp + Td, H=4)
+    t = {n: f.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "u", "w", "d",
+                                         "conv_q", "conv_k", "conv_v")}
+    conv = (t["conv_q"], t["conv_k"], t["conv_v"])
+    s0 = torch.from_numpy(f.base.initial_state).to(dev())
+    cut = lambda x, a, b: x[:, a:b].contiguous()
+    o_pre, S = R.chunk_fwd_fused(cut(t["q"], 0, W - 1 + Tp), cut(t["k"], 0, W - 1 + Tp),
+                                 cut(t["v"], 0, W - 1 + Tp), cut(t["g"], 0, Tp), cut(t["tau"], 0, Tp),
+                                 u=cut(t["u"], 0, Tp), w=t["w"], d=t["d"], conv=conv,
+                                 initial_state=s0, output_final_state=True)
+    outs = [o_pre.cpu().numpy()]
+    for s in range(Td):
+        tok = Tp + s
+        win = [cut(t[n], tok, tok + W) for n in ("q", "k", "v")]
+        o = R.decode_step_fused(*win, t["g"][:, tok].contiguous(), t["tau"][:, tok].contiguous(), S,
+                                u=t["u"][:, tok].contiguous(), w=t["w"], d=t["d"], conv=conv)
+        outs.append(o.cpu().numpy()[:, None])
+    torch.cuda.synchronize()
+    got = np.concatenate(outs, axis=1)
+    ro, rs = oracle.fwd_fused(f.f32("q"), f.f32("k"), f.f32("v"), f.f32("g"), f.f32("tau"),
+                              u=f.f32("u"), w=f.f32("w"), d=f.d,
+                              conv=(f.conv_q, f.conv_k, f.conv_v), initial_state=f.base.initial_state)
+    eo = oracle.rel_to_rms_error(got, ro)
+    ed = oracle.rel_to_rms_error(got[:, Tp:], ro[:, Tp:])
+    es = oracle.rel_to_rms_error(S.cpu().numpy(), rs)
+    print(f"[prefill+decode fused] out {eo:.2e} decode part {ed:.2e} state {es:.2e}", flush=True)
+    assert eo <= 1e-2 and ed <= 1e-2 and es <= 1e-2
+
+
+@pytest.mark.parametrize("use_conv,use_u,use_d", [(False, True, False), (True, False, True),
+                                                  (False, False, True)])
+def test_decode_fused_one_step(R, use_conv, use_u, use_d):
+    W = 3
+    f = D.make_fused("decode_batch", conv_width=W, B=16, T=1, H=8)
+    st = f.base.initial_state
+    t = {n: f.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "beta_hat", "u", "w", "d",
+                                         "conv_q", "conv_k", "conv_v")}
+    if use_conv:
+        q, k, v = t["q"], t["k"], t["v"]                       # [N, W, H, D] windows
+        rq, rk, rv = f.f32("q"), f.f32("k"), f.f32("v")
+        conv = (t["conv_q"], t["conv_k"], t["conv_v"])
+        rconv = (f.conv_q, f.conv_k, f.conv_v)
+    else:
+        q, k, v = (t[n][:, W - 1].contiguous() for n in ("q", "k", "v"))
+        rq, rk, rv = (f.f32(n)[:, W - 1] for n in ("q", "k", "v"))
+        conv = rconv = None
+    S = torch.from_numpy(st).to(dev())
+    o = R.decode_step_fused(q, k, v, t["g"][:, 0].contiguous(), t["tau"][:, 0].contiguous(), S,
+                            beta_hat=None if use_u else t["beta_hat"][:, 0].contiguous(),
+                            u=t["u"][:, 0].contiguous() if use_u else None,
+                            w=t["w"] if use_u else None, d=t["d"] if use_d else None, conv=conv)
+    torch.cuda.synchronize()
+    ro, rs = oracle.decode_fused(rq, rk, rv, f.f32("g")[:, 0], f.f32("tau")[:, 0], st,
+                                 beta_hat=None if use_u else f.f32("beta_hat")[:, 0],
+                                 u=f.f32("u")[:, 0] if use_u else None,
+                                 w=f.f32("w") if use_u else None, d=f.d if use_d else None,
+                                 conv=rconv)
+    eo = oracle.rel_to_rms_error(o.cpu().numpy(), ro)
+    es = oracle.rel_to_rms_error(S.cpu().numpy(), rs)
+    print(f"[decode fused conv={use_conv} u={use_u} d={use_d}] out {eo:.2e} state {es:.2e}", flush=True)
+    assert eo <= 1e-2 and es <= 1e-2
