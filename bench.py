@@ -4,24 +4,26 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 A step is one chunkwise-parallel forward (rodimus_ddts_chunk_fwd) over one
-batch of the 130M-scale layer workload: B=8 sequences x T=2048 tokens x H=12
-heads, dk=64, dv=128, bf16 inputs, fp32 outputs.  Inputs are seeded synthetic
-tensors, resident in HBM before the timed region; the step cycles through
-``--rotate`` copies of them so that the 256 MB last-level cache cannot serve a
-batch from the previous step.  After the chunk steps the same run times
-``--decode-steps`` back-to-back decode steps over 256 x 16 resident fp32
-states (the batched decode workload) and reports the state bandwidth, once on
-one resident state batch (which the 256 MB last-level cache partly holds) and
-once cold, rotating over 12 state batches (1.6 GB).
+batch of the long-context prefill workload, the largest that runs on one GPU:
+B=1 sequence x T=65536 tokens x H=16 heads, dk=64, dv=128, bf16 inputs, a
+nonzero fp32 initial state, fp32 outputs.  The library splits each sequence
+into segments (a transfer pass, an ordered combine, an output pass).  Inputs
+are seeded synthetic tensors, resident in HBM before the timed region; the
+step cycles through ``--rotate`` copies of them.
 
-One JSON line on stdout:  value = tokens/s of the chunk forward (B*T tokens
-per step), the roofline of the chunk kernel (HBM-bound: algorithmic bytes per
-launch / its HIP-event-timed duration), the forward on the other workloads
-(``--other-workloads``: the 1.6B-scale layer and the 64K-token prefill, both
-segmented; time per call and algorithmic bandwidth), the decode-step bandwidth, the
-backward (rodimus_ddts_chunk_bwd) on the same batch, a 24K-token prefill
-followed by decode steps from its carried state, and the fp64 CPU oracle
-timed on this host on the same workload (a reported baseline).
+One JSON line on stdout:  value = tokens/s of the forward (B*T tokens per
+step, whole call).  ``roofline`` is for the dominant kernel of the call (the
+output pass): the call's algorithmic bytes (every input read once, the output
+written once, the initial state read once; the output pass is the one launch
+that reads all of them) over that pass's average duration, timed live with
+HIP events that the library records on its own stream around each pass
+(rodimus_trace_forward_events), next to the whole call's fraction.  The same
+line carries the forward on the other workloads (the 130M and 1.6B layers,
+each with its own fraction), the 130M layer fed low-rank beta_hat factors
+(the fused path, and the bytes it saves), the decode-step bandwidth, the
+backward (rodimus_ddts_chunk_bwd) on the 130M layer, a 24K-token prefill
+followed by decode steps from its carried state, and the fp64 CPU oracle timed
+on this host (all threads and one thread; a reported baseline).
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "DDTS chunk-fwd tokens/s + % MFMA/HBM roofline; decode-step state GB/s"
 NAMES = ("q", "k", "v", "g", "tau", "beta_hat")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer130m_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_long_prefill_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_linear_attention_rodimus_amd", "csrc", "chunk_kernel.h")
 
 
@@ -57,25 +59,101 @@ def decode_algorithmic(N, H, dk, dv, in_bytes=2):
     return by, 5 * N * H * dk * dv
 
 
-def kernel_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def kernel_traffic(key):
+    """HBM bytes per launch of one pass (``key``) from the committed rocprofv3
+    counter summary, or None when the kernel source changed since the
+    counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
         sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
         if rec.get("kernel_source_sha256") != sha:
             return None
-        return rec["hbm_bytes_per_launch"]
-    except (OSError, ValueError, KeyError):
+        return rec["passes"][key]["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError, TypeError):
         return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_passes(R, call, n, stream):
+    """Average duration (us) of each pass of ``n`` forward calls, from the
+    events the library records around its launches."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    for row in evs:                      # create the events before handing them over
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n):
+        R.trace_forward_events(evs[i])
+        call(i)
+    R.trace_forward_events(None)
+    torch.cuda.synchronize()
+    return evs
+
+
+def forward_sets(R, D, name, dev, rotate):
+    """``rotate`` resident copies of a workload's inputs, outputs and state."""
+    import torch
+    wl = D.WORKLOADS[name]
+    x = D.make(name)
+    sets = []
+    for r in range(max(1, rotate)):
+        t = [x.torch(n, dev) for n in NAMES]
+        if r:
+            t = [a.clone() for a in t]
+        out = torch.empty(wl.B, wl.T, wl.H, wl.dv, device=dev)
+        fs = torch.empty(wl.B, wl.H, wl.dk, wl.dv, device=dev) if wl.final_state else None
+        s0 = torch.from_numpy(x.initial_state).to(dev) if x.initial_state is not None else None
+        sets.append((t, s0, out, fs))
+    wsb = R.workspace_bytes(wl.B, wl.T, wl.H, wl.dk, wl.dv)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    return x, sets, ws, wsb
+
+
+def warm(step, seconds, min_steps=10):
+    """Run ``step`` until it has kept the GPU busy for ``seconds`` (its clocks
+    rise over the first ~20 ms under load)."""
+    import torch
+    i = 0
+    tw = time.perf_counter()
+    while i < min_steps or time.perf_counter() - tw < seconds:
+        step(i)
+        i += 1
+        if i % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def timed(step, n, stream):
+    """Average time (us) of ``n`` back-to-back calls, one event pair around
+    them on ``stream`` (events between the calls would stall the queue)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--rotate", type=int, default=3, help="input copies cycled over steps")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=2, help="input copies cycled over steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--bwd-steps", type=int, default=20, help="timed backward calls (0: skip)")
     ap.add_argument("--serve-steps", type=int, default=100,
@@ -83,10 +161,12 @@ def main():
     ap.add_argument("--serve-prefill", type=int, default=24576)
     ap.add_argument("--serve-batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="layer130m")
-    ap.add_argument("--other-workloads", default="layer1p6b,long_prefill",
+    ap.add_argument("--workload", default="long_prefill")
+    ap.add_argument("--other-workloads", default="layer130m,layer1p6b",
                     help="comma-separated forward workloads timed after the main one "
                          "('none': skip)")
+    ap.add_argument("--fused-steps", type=int, default=20,
+                    help="timed calls of the 130M layer fed low-rank beta_hat factors (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times), "
                          "to scale the HBM byte counters of a profiler run")
@@ -115,20 +195,11 @@ def main():
     import gated_linear_attention_rodimus_amd as R
 
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     wl = D.WORKLOADS[args.workload]
     B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
-    x = D.make(args.workload)
-    sets = []
-    for r in range(max(1, args.rotate)):
-        t = [x.torch(n, dev) for n in NAMES]
-        if r:
-            t = [a.clone() for a in t]
-        out = torch.empty(B, T, H, dv, device=dev)
-        fs = torch.empty(B, H, dk, dv, device=dev) if wl.final_state else None
-        s0 = torch.from_numpy(x.initial_state).to(dev) if x.initial_state is not None else None
-        sets.append((t, s0, out, fs))
-    wsb = R.workspace_bytes(B, T, H, dk, dv)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) if wsb else None
+    x, sets, ws, wsb = forward_sets(R, D, args.workload, dev, args.rotate)
+    plan = R.chunk_fwd_plan(B, T, H, dk, dv)
     torch.cuda.synchronize()
 
     def step(i):
@@ -136,26 +207,16 @@ def main():
         R.chunk_fwd(*t, initial_state=s0, out=out, final_state=fs, workspace=ws)
 
     # warm-up: the W steps asked for, continued until the steps have kept the
-    # GPU busy for 25 ms (its clocks rise over the first ~20 ms under load:
-    # 119 us per step measured after 5 warm-up steps, 105-106 us after 200 or
-    # more)
+    # GPU busy for 25 ms
     n_warm = 0
-    tw = time.perf_counter()
     for _ in range(args.warmup):
         step(n_warm)
         n_warm += 1
     torch.cuda.synchronize()
-    while time.perf_counter() - tw < 0.025:
-        for _ in range(10):
-            step(n_warm)
-            n_warm += 1
-        torch.cuda.synchronize()
-    # the K launches go back to back on the library's stream (the current
-    # one); one event pair brackets them, so the average launch duration is
-    # (end - start) / K, gaps between launches included.  Events recorded
-    # between the launches themselves stall the queue (~14 us per step here)
-    # and would be timed as part of the kernel.
-    stream = torch.cuda.current_stream(dev)
+    n_warm += warm(step, 0.025)
+    # the K timed steps: back to back on the library's stream (the current
+    # one), a synchronize on each side for the wall clock and one event pair
+    # for the device time
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -166,67 +227,65 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-    tokens = B * T
-    value = tokens * args.steps / wall
+    call_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    value = B * T * args.steps / wall
 
-    C = 64
+    C = plan["chunk"]
     abytes, aflops = chunk_algorithmic(B, T, H, dk, dv, C, state_in=x.initial_state is not None,
                                        state_out=wl.final_state)
-    achieved = abytes / avg_launch_s / 1e9
-    traffic = kernel_traffic()
+    # each pass of further calls, timed by the events the library records
+    # around its own launches on its stream
+    n_pass = max(5, args.steps)
+    evs = time_passes(R, step, n_pass, stream)
+    segmented = plan["segments"] > 1
+    names = ("transfer", "combine", "output") if segmented else ("sweep",)
+    passes = {}
+    for j, nm in enumerate(names):
+        passes[nm] = float(np.mean([row[j].elapsed_time(row[j + 1]) * 1e3 for row in evs]))
+    dom = max(passes, key=passes.get)
+    dom_us = passes[dom]
+    ker = (f"chunk_fwd_kernel<{dk},{plan['dv_tile']},{C},bf16,outputs>"
+           + (" (output pass of the segmented forward)" if segmented else " (one sweep)"))
+    achieved = abytes / (dom_us * 1e-6) / 1e9
+    traffic = kernel_traffic(dom)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "chunk_fwd_kernel<64,64,64,bf16,outputs>" if wsb == 0 else "chunk_fwd (segmented)",
+                "kernel": ker, "dominant_pass": dom,
                 "algorithmic_bytes_per_launch": abytes,
-                "launch_us": round(avg_launch_s * 1e6, 2),
-                "mfma": {"achieved_tflops": round(aflops / avg_launch_s / 1e12, 2),
+                "launch_us": round(dom_us, 2),
+                "passes_us": {k: round(v, 2) for k, v in passes.items()},
+                "call_us": round(call_us, 2),
+                "call_frac": round(abytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "traffic_over_algorithmic": (round(traffic / abytes, 4) if traffic else None),
+                "mfma": {"achieved_tflops": round(aflops / (call_us * 1e-6) / 1e12, 2),
                          "peak_tflops": BF16_PEAK_TFLOPS,
-                         "frac": round(aflops / avg_launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "algorithmic_flops_per_launch": aflops}}
+                         "frac": round(aflops / (call_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops_per_call": aflops}}
+    main_parity_sample = sets[0]
+    del sets
+    torch.cuda.empty_cache()
 
     # ---------------- the other forward workloads (the same timing: settled
-    # clocks, one event pair around back-to-back calls, two rotating input sets)
+    # clocks, one event pair around back-to-back calls, rotating input sets)
     others = {}
-    names = [] if args.other_workloads in ("", "none") else args.other_workloads.split(",")
-    for name in names:
+    names_o = [] if args.other_workloads in ("", "none") else args.other_workloads.split(",")
+    for name in names_o:
         if name == args.workload:
             continue
         owl = D.WORKLOADS[name]
-        ox = D.make(name)
-        osets = []
-        for r in range(2):
-            t = [ox.torch(n, dev) for n in NAMES]
-            if r:
-                t = [a.clone() for a in t]
-            o_out = torch.empty(owl.B, owl.T, owl.H, owl.dv, device=dev)
-            o_fs = torch.empty(owl.B, owl.H, owl.dk, owl.dv, device=dev) if owl.final_state else None
-            o_s0 = torch.from_numpy(ox.initial_state).to(dev) if ox.initial_state is not None else None
-            osets.append((t, o_s0, o_out, o_fs))
-        owsb = R.workspace_bytes(owl.B, owl.T, owl.H, owl.dk, owl.dv)
-        ows = torch.empty(max(owsb, 1), dtype=torch.uint8, device=dev) if owsb else None
+        ox, osets, ows, owsb = forward_sets(R, D, name, dev, 3)
 
         def ostep(i):
-            t, s0_, out_, fs_ = osets[i % 2]
+            t, s0_, out_, fs_ = osets[i % len(osets)]
             R.chunk_fwd(*t, initial_state=s0_, out=out_, final_state=fs_, workspace=ows)
 
-        i = 0
-        tw = time.perf_counter()
-        while i < 10 or time.perf_counter() - tw < 0.025:
-            ostep(i)
-            i += 1
-            torch.cuda.synchronize()
-        k = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for j in range(k):
-            ostep(j)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / k
-        oby, _ = chunk_algorithmic(owl.B, owl.T, owl.H, owl.dk, owl.dv, 64,
-                                   state_in=ox.initial_state is not None, state_out=owl.final_state)
+        warm(ostep, 0.025)
+        us = timed(ostep, 20, stream)
+        oplan = R.chunk_fwd_plan(owl.B, owl.T, owl.H, owl.dk, owl.dv)
+        oby, ofl = chunk_algorithmic(owl.B, owl.T, owl.H, owl.dk, owl.dv, oplan["chunk"],
+                                     state_in=ox.initial_state is not None,
+                                     state_out=owl.final_state)
         others[name] = {"shape": f"B={owl.B} T={owl.T} H={owl.H} dk={owl.dk} dv={owl.dv} bf16 inputs"
                                  + (", initial state" if ox.initial_state is not None else "")
                                  + (", returns S_T" if owl.final_state else ""),
@@ -235,9 +294,43 @@ def main():
                         "algorithmic_bytes_per_call": oby,
                         "algorithmic_GBps": round(oby / us / 1e3, 1),
                         "frac_hbm": round(oby / us / 1e3 / HBM_PEAK_GBPS, 4),
-                        "workspace_bytes": owsb,
-                        "plan": R.chunk_fwd_plan(owl.B, owl.T, owl.H, owl.dk, owl.dv)}
+                        "workspace_bytes": owsb, "plan": oplan}
         del osets, ows
+        torch.cuda.empty_cache()
+
+    # ---------------- the fused path: the 130M layer fed its rank-16 beta_hat
+    # factors u, w (beta_hat = sigmoid(u w) formed in the chunk load)
+    fused = None
+    if args.fused_steps > 0:
+        fwl = D.WORKLOADS["layer130m"]
+        fx = D.make_fused("layer130m", conv_width=1)
+        fsets = []
+        for r in range(3):
+            ft = {n: fx.torch(n, dev) for n in ("q", "k", "v", "g", "tau", "u", "w")}
+            if r:
+                ft = {n: a.clone() for n, a in ft.items()}
+            fsets.append((ft, torch.empty(fwl.B, fwl.T, fwl.H, fwl.dv, device=dev)))
+
+        def fstep(i):
+            ft, fo = fsets[i % 3]
+            R.chunk_fwd_fused(ft["q"], ft["k"], ft["v"], ft["g"], ft["tau"], u=ft["u"], w=ft["w"],
+                              out=fo)
+
+        warm(fstep, 0.025)
+        fus = timed(fstep, args.fused_steps, stream)
+        ntok = fwl.B * fwl.T * fwl.H
+        r_ = fx.u.shape[-1]
+        dense_by, _ = chunk_algorithmic(fwl.B, fwl.T, fwl.H, fwl.dk, fwl.dv, 64)
+        fby = dense_by - ntok * 2 * fwl.dv * 2 + ntok * r_ * 2 + fwl.H * r_ * fwl.dv * 2
+        fused = {"workload": f"layer130m B={fwl.B} T={fwl.T} H={fwl.H} dk={fwl.dk} dv={fwl.dv} bf16, "
+                             f"beta_hat = sigmoid(u w) from rank-{r_} factors inside the kernel",
+                 "us_per_call": round(fus, 2),
+                 "tokens_per_s": round(fwl.B * fwl.T / (fus * 1e-6), 1),
+                 "algorithmic_bytes_per_call": fby,
+                 "bytes_saved_vs_dense_beta_hat": dense_by - fby,
+                 "algorithmic_GBps": round(fby / fus / 1e3, 1),
+                 "frac_hbm": round(fby / fus / 1e3 / HBM_PEAK_GBPS, 4)}
+        del fsets
         torch.cuda.empty_cache()
 
     # ---------------- decode: back-to-back steps over resident states
@@ -251,25 +344,14 @@ def main():
         for i in range(10):
             R.decode_step(*dins[i % len(dins)], S, out=o)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.decode_steps):
-            R.decode_step(*dins[i % len(dins)], S, out=o)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        us = timed(lambda i: R.decode_step(*dins[i % len(dins)], S, out=o), args.decode_steps, stream)
         dbytes, dflops = decode_algorithmic(N, Hd, dkd, dvd)
         # cold variant: state batches in rotation whose total (12 x 134 MB) exceeds
         # the 256 MB last-level cache, as when every layer of a model keeps a state
         n_cold = 12
         Ss = [S] + [S.clone() for _ in range(n_cold - 1)]
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.decode_steps):
-            R.decode_step(*dins[i % len(dins)], Ss[i % n_cold], out=o)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us_cold = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        us_cold = timed(lambda i: R.decode_step(*dins[i % len(dins)], Ss[i % n_cold], out=o),
+                        args.decode_steps, stream)
         decode = {"workload": f"decode_batch N{N} H{Hd} dk{dkd} dv{dvd} bf16 inputs, fp32 state",
                   "steps": args.decode_steps, "us_per_step": round(us, 2),
                   "algorithmic_bytes_per_step": dbytes,
@@ -281,36 +363,34 @@ def main():
                   "cold_algorithmic_GBps": round(dbytes / us_cold / 1e3, 1),
                   "cold_frac_hbm": round(dbytes / us_cold / 1e3 / HBM_PEAK_GBPS, 4),
                   "tokens_per_s": round(N / (us * 1e-6), 1)}
+        del Ss, S
+        torch.cuda.empty_cache()
 
-    # ---------------- backward of the chunk forward on the same batch
+    # ---------------- backward of the chunk forward on the 130M layer
     backward = None
     if args.bwd_steps > 0:
+        bwl = D.WORKLOADS["layer130m"]
+        Bb, Tb, Hb, dkb, dvb = bwl.B, bwl.T, bwl.H, bwl.dk, bwl.dv
+        bx = D.make("layer130m")
+        bt = [bx.torch(n, dev) for n in NAMES]
         rng = np.random.default_rng(2)
-        d_out = torch.from_numpy(rng.standard_normal((B, T, H, dv), dtype=np.float32)).to(dev)
-        bwsb = R.bwd_workspace_bytes(B, T, H, dk, dv)
+        d_out = torch.from_numpy(rng.standard_normal((Bb, Tb, Hb, dvb), dtype=np.float32)).to(dev)
+        bwsb = R.bwd_workspace_bytes(Bb, Tb, Hb, dkb, dvb)
         bws = torch.empty(max(bwsb, 1), dtype=torch.uint8, device=dev)
-        t0_, s0_ = sets[0][0], sets[0][1]
-        tw = time.perf_counter()                 # warm-up: 50 ms of this call
-        while time.perf_counter() - tw < 0.05:
-            for _ in range(2):
-                R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
-            torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.bwd_steps):
-            R.chunk_bwd(*t0_, d_out, initial_state=s0_, workspace=bws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bus = e0.elapsed_time(e1) * 1e3 / args.bwd_steps
-        ntok = B * T * H
-        bbytes = ntok * ((4 * dk + 2 * dv) * 2 + 4 * dv + (4 * dk + 2 * dv) * 4)
+        bstep = lambda i: R.chunk_bwd(*bt, d_out, workspace=bws)
+        warm(bstep, 0.05, min_steps=2)
+        bus = timed(bstep, args.bwd_steps, stream)
+        ntok = Bb * Tb * Hb
+        bbytes = ntok * ((4 * dkb + 2 * dvb) * 2 + 4 * dvb + (4 * dkb + 2 * dvb) * 4)
         backward = {"entry": "rodimus_ddts_chunk_bwd (state sweeps + chunk gradients)",
-                    "workload": args.workload, "calls": args.bwd_steps,
-                    "us_per_call": round(bus, 1), "tokens_per_s": round(B * T / (bus * 1e-6), 1),
+                    "workload": "layer130m", "calls": args.bwd_steps,
+                    "us_per_call": round(bus, 1), "tokens_per_s": round(Bb * Tb / (bus * 1e-6), 1),
                     "algorithmic_bytes_per_call": bbytes,
                     "algorithmic_GBps": round(bbytes / bus / 1e3, 1),
                     "frac_hbm": round(bbytes / bus / 1e3 / HBM_PEAK_GBPS, 4),
                     "workspace_bytes": bwsb}
+        del bt, bws, d_out
+        torch.cuda.empty_cache()
 
     # ---------------- prefill then batched decode from the carried state
     serving = None
@@ -370,31 +450,42 @@ def main():
                    "decode_graph_us_per_step": round(dec_graph_us, 2),
                    "decode_graph_tokens_per_s": round(Bs / (dec_graph_us * 1e-6), 1)}
 
-    # ---------------- CPU baseline: the fp64 oracle on this host, same workload
+    # ---------------- CPU baseline: the fp64 oracle on this host, a bounded
+    # sample of the same workload (whole sequences of some heads), once on all
+    # threads and once on one thread; tokens/s counts B*T tokens of all H heads
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
         import oracle
         nthreads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-        # sample: the whole batch (all sequences and heads, whole length), in
-        # repeated passes until about 10 s of CPU work have been timed
-        Bs = B
-        ins = [np.ascontiguousarray(x.f32(n)[:Bs]) for n in NAMES]
-        s0 = None if x.initial_state is None else x.initial_state[:Bs]
-        passes = 0
-        c0 = time.perf_counter()
-        ro = None
-        while passes == 0 or time.perf_counter() - c0 < 10.0:
-            o_, _ = oracle.fwd(*ins, s0, nthreads=nthreads)
-            if ro is None:
-                ro = o_
-            passes += 1
-        cs = time.perf_counter() - c0
-        cpu = {"value": round(passes * Bs * T / cs, 1), "unit": "tokens/s",
-               "cores": oracle.fwd.last_threads, "kind": "oracle",
-               "sample": f"{Bs} of {B} sequences x {T} tokens x {H} heads of the same workload, "
-                         f"{passes} passes, fp64 C oracle, {cs:.1f} s"}
-        gpu_o = sets[0][2][:Bs].cpu().numpy()
+        hs = min(H, max(1, nthreads))          # heads in the sample: one per thread
+        Ts = min(T, 16384)
+        ins = [np.ascontiguousarray(x.f32(n)[:1, :Ts, :hs]) for n in NAMES]
+        s0 = None if x.initial_state is None else np.ascontiguousarray(x.initial_state[:1, :hs])
+
+        def rate(threads, heads, budget):
+            sl = [np.ascontiguousarray(a[:, :, :heads]) for a in ins]
+            s0s = None if s0 is None else np.ascontiguousarray(s0[:, :heads])
+            passes, c0, ro = 0, time.perf_counter(), None
+            while passes == 0 or time.perf_counter() - c0 < budget:
+                o_, _ = oracle.fwd(*sl, s0s, nthreads=threads)
+                ro = o_ if ro is None else ro
+                passes += 1
+            cs = time.perf_counter() - c0
+            # token-heads per second, expressed as tokens of all H heads
+            return passes * Ts * heads / cs / H, oracle.fwd.last_threads, passes, cs, ro
+
+        v_all, used, p_all, c_all, ro = rate(nthreads, hs, 10.0)
+        v_one, _, p_one, c_one, _ = rate(1, 1, 5.0)
+        cpu = {"value": round(v_all, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+               "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+               "one_thread": {"value": round(v_one, 1), "unit": "tokens/s", "cores": 1,
+                              "sample": f"1 head x {Ts} tokens, {p_one} passes, {c_one:.1f} s"},
+               "sample": f"{args.workload}: first {Ts} tokens of {hs} of {H} heads (B=1), "
+                         f"{p_all} passes, fp64 C oracle, {c_all:.1f} s; tokens/s counts "
+                         f"token-heads / {H}"}
+        gpu_o = main_parity_sample[2][:1, :Ts, :hs].cpu().numpy()
+        # the GPU's first Ts tokens depend only on the first Ts tokens and S_0
         parity = {"max_abs_over_rms": oracle.rel_to_rms_error(gpu_o, ro), "bar": 1e-2,
                   "sample": "the CPU-baseline sample"}
 
@@ -404,11 +495,16 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"{args.workload}: B={B} T={T} H={H} dk={dk} dv={dv} "
-                                   f"bf16 inputs, fp32 out/state, chunk {C}",
+                                   f"bf16 inputs, fp32 out/state"
+                                   + (", initial state" if x.initial_state is not None else "")
+                                   + (", returns S_T" if wl.final_state else "")
+                                   + f"; plan: chunk {C}, dv tile {plan['dv_tile']}, "
+                                     f"{plan['segments']} segments",
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
-                       "rotating_input_sets": len(sets), "parallelism": "single GPU"},
+                       "rotating_input_sets": args.rotate, "parallelism": "single GPU"},
             "roofline": roofline, "cpu_baseline": cpu, "other_forward": others or None,
-            "decode": decode, "backward": backward, "serving": serving, "parity": parity}
+            "fused": fused, "decode": decode, "backward": backward, "serving": serving,
+            "parity": parity}
     print(json.dumps(line), flush=True)
 
 

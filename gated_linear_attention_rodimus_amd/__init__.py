@@ -23,7 +23,7 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "chunk_fwd_no_alloc", "chunk_bwd", "decode_step",
-           "decode_step_fused", "workspace_bytes", "fused_workspace_bytes",
+           "decode_step_fused", "workspace_bytes", "fused_workspace_bytes", "trace_forward_events",
            "bwd_workspace_bytes", "chunk_fwd_plan", "STATIC_SCRATCH_BYTES",
            "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_decode_step_fused.restype = i
         L.rodimus_ddts_decode_step_fused.argtypes = ([i] * 5 + [vp] * 6 + [ctypes.POINTER(_Fused)]
                                                      + [vp] * 3)
+        L.rodimus_trace_forward_events.restype = i
+        L.rodimus_trace_forward_events.argtypes = [vp, i]
         L.rodimus_ddts_decode_step.restype = i
         L.rodimus_ddts_decode_step.argtypes = [i] * 5 + [vp] * 8 + [vp]
         L.rodimus_ddts_chunk_bwd_workspace_bytes.restype = sz
@@ -371,6 +373,23 @@ def chunk_fwd_no_alloc(q, k, v, g, tau, beta_hat, out, initial_state=None, final
     if st != OK:
         raise RodimusError(st, "rodimus_ddts_chunk_fwd_static_scratch")
     return out, final_state
+
+
+def trace_forward_events(events):
+    """Record the given 4 torch.cuda.Events around the launches of this host
+    thread's following forward calls (rodimus_trace_forward_events); None
+    stops.  One sweep: events 0 and 1 bracket the kernel; segmented: 0 | transfer
+    | 1 | combine | 2 | output | 3."""
+    if events is None:
+        st = lib().rodimus_trace_forward_events(None, 0)
+    else:
+        if len(events) != 4:
+            raise ValueError("trace_forward_events needs 4 events")
+        handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        trace_forward_events._keep = handles
+        st = lib().rodimus_trace_forward_events(handles, 4)
+    if st != OK:
+        raise RodimusError(st, "rodimus_trace_forward_events")
 
 
 def decode_step(q, k, v, g, tau, beta_hat, state, out=None):

@@ -298,6 +298,14 @@ rodimus_status chunk_fwd_check(
     return RODIMUS_OK;
 }
 
+// Tracing aid: the calling host thread's pass events (rodimus_trace_forward_events).
+thread_local hipEvent_t *trace_ev = nullptr;
+
+hipError_t trace(int i, hipStream_t stream)
+{
+    return trace_ev ? hipEventRecord(trace_ev[i], stream) : hipSuccess;
+}
+
 // The launches of a checked forward call; `workspace` holds at least
 // P.ws_bytes bytes when P.segments > 1.
 rodimus_status chunk_fwd_launch(
@@ -333,7 +341,9 @@ rodimus_status chunk_fwd_launch(
         Lc.out = out;
         Lc.s_out = final_state; Lc.s_out_bh_stride = sz; Lc.s_out_seg_stride = 0;
         Lc.s_out_last_only = 0;
+        if (trace(0, stream) != hipSuccess) return RODIMUS_ERR_HIP;
         e = launch_chunk(Lc, stream);
+        if (e == hipSuccess) e = trace(1, stream);
         return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
     }
     // segmented: (1) transfers from a zero state over the chunks before the
@@ -349,9 +359,12 @@ rodimus_status chunk_fwd_launch(
     Lc.s_out = ws_ds; Lc.s_out_bh_stride = (long long)slots * sz; Lc.s_out_seg_stride = sz;
     Lc.s_out_last_only = 0;
     Lc.gam_out = ws_gam; Lc.gam_bh_stride = (long long)slots * dk;
+    if (trace(0, stream) != hipSuccess) return RODIMUS_ERR_HIP;
     e = launch_chunk(Lc, stream);
+    if (e == hipSuccess) e = trace(1, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
     e = launch_segment_combine(B * H, n_seg, per, slots, dk, dv, initial_state, ws_ds, ws_gam, stream);
+    if (e == hipSuccess) e = trace(2, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
     Lc.n_seg = n_seg; Lc.chunks_per_seg = P.chunks_per_seg; Lc.mode = 0;
     Lc.s_in = ws_ds; Lc.s_in_bh_stride = (long long)slots * sz; Lc.s_in_seg_stride = sz;
@@ -360,6 +373,7 @@ rodimus_status chunk_fwd_launch(
     Lc.s_out_last_only = 1;
     Lc.gam_out = nullptr;
     e = launch_chunk(Lc, stream);
+    if (e == hipSuccess) e = trace(3, stream);
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
 }
 
@@ -389,6 +403,17 @@ hipError_t scratch_ptr(void **p)
 }  // namespace
 
 extern "C" {
+
+rodimus_status rodimus_trace_forward_events(hipEvent_t *events, int count)
+{
+    if (count == 0) {
+        trace_ev = nullptr;
+        return RODIMUS_OK;
+    }
+    if (count != 4 || !events) return RODIMUS_ERR_INVALID_ARG;
+    trace_ev = events;
+    return RODIMUS_OK;
+}
 
 rodimus_status rodimus_ddts_chunk_fwd_ex(
     int B, int T, int H, int dk, int dv, int chunk, int segments, rodimus_dtype in_dtype,

@@ -171,6 +171,19 @@ rodimus_status rodimus_ddts_chunk_fwd_static_scratch(
     const float *initial_state, float *out, float *final_state, hipStream_t stream);
 
 /*
+ * Tracing aid (the profiler's view of one forward call, on its own stream):
+ * until called again with count = 0, every forward call made by the calling
+ * host thread records the caller's events (hipEventCreate) on its stream
+ * around its launches: one sweep: events[0] before the launch, events[1]
+ * after it; segmented: events[0] before the transfer pass, events[1] after
+ * it, events[2] after the ordered combine, events[3] after the output pass.
+ * count must be 4 (RODIMUS_ERR_INVALID_ARG otherwise), or 0 to stop.  The
+ * events array must stay valid while set.  No event is recorded by a call
+ * that fails its checks.
+ */
+rodimus_status rodimus_trace_forward_events(hipEvent_t *events, int count);
+
+/*
  * How rodimus_ddts_chunk_fwd_ex runs for these arguments and input dtype:
  *   chunk            tokens per chunk (16, 32 or 64);
  *   dv_tile          dv columns per workgroup;

@@ -340,3 +340,15 @@ def test_static_scratch_entry_rejects_plans_beyond_its_buffer():
                                                  *(vp(p) for p in ptrs), None, vp(ptrs[0]), None,
                                                  None)
     assert st == R.ERR_INVALID_ARG            # out overlaps q
+
+
+def test_trace_events_argument_checks():
+    """The tracing aid takes exactly four events, or none to stop; nothing
+    else reaches the runtime."""
+    L = R.lib()
+    assert L.rodimus_trace_forward_events(None, 0) == R.OK
+    assert L.rodimus_trace_forward_events(None, 4) == R.ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    assert L.rodimus_trace_forward_events(arr, 3) == R.ERR_INVALID_ARG
+    assert L.rodimus_trace_forward_events(arr, 4) == R.OK
+    assert L.rodimus_trace_forward_events(None, 0) == R.OK

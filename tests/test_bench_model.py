@@ -37,3 +37,26 @@ def test_decode_bytes():
     n = 256 * 16
     assert by == n * (2 * 64 * 128 * 4 + (4 * 64 + 2 * 128) * 2 + 128 * 4) == 274_726_912
     assert fl == 5 * n * 64 * 128
+
+
+def test_pass_traffic_record_is_consistent():
+    """The committed counter summary of the long prefill: per-pass HBM bytes
+    are FETCH_SIZE x the copy scale + WRITE_SIZE, their sum is the call's,
+    and the bench reads the output pass's figure only while the kernel
+    source is the one the counters were taken on."""
+    import hashlib
+    import json
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    total = 0
+    for name, p in rec["passes"].items():
+        hbm = p["fetch_size_kib_per_dispatch"] * 1024 * rec["fetch_scale"] + \
+            p["write_size_kib_per_dispatch"] * 1024 * rec["write_scale"]
+        assert abs(hbm - p["hbm_bytes_per_launch"]) / hbm < 1e-4, name
+        total += p["hbm_bytes_per_launch"]
+    assert total == rec["call_hbm_bytes"]
+    assert rec["passes"]["output"]["algorithmic_bytes_per_launch"] == \
+        bench.chunk_algorithmic(1, 65536, 16, 64, 128, 32, state_in=True)[0]
+    sha = hashlib.sha256(open(bench.KERNEL_SRC, "rb").read()).hexdigest()
+    got = bench.kernel_traffic("output")
+    assert got == (rec["passes"]["output"]["hbm_bytes_per_launch"]
+                   if sha == rec["kernel_source_sha256"] else None)

@@ -150,3 +150,29 @@ def test_decode_step_propagates_nan_and_inf(R):
         assert bad.any()
         assert np.array_equal(bad, ~np.isfinite(g_))
         assert oracle.rel_to_rms_error(g_[~bad], r_[~bad]) <= 1e-2
+
+
+def test_trace_events_bracket_the_passes(R):
+    """The library's pass events: ordered in time, their spans add up to the
+    call, and tracing leaves the results unchanged (segmented and one-sweep
+    shapes)."""
+    dev = torch.device("cuda:0")
+    for x, s0 in ((D.make("long_prefill", T=20000, H=4), True), (D.make("layer130m", B=2, T=500), False)):
+        t = [x.torch(n, dev) for n in NAMES]
+        s0d = torch.from_numpy(x.initial_state).to(dev) if s0 else None
+        o_ref, _ = R.chunk_fwd(*t, initial_state=s0d)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record()
+        torch.cuda.synchronize()
+        R.trace_forward_events(ev)
+        try:
+            o, _ = R.chunk_fwd(*t, initial_state=s0d)
+        finally:
+            R.trace_forward_events(None)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
+        seg = R.chunk_fwd_plan(*[x.wl.B, x.wl.T, x.wl.H, 64, 128])["segments"] > 1
+        spans = [ev[j].elapsed_time(ev[j + 1]) for j in range(3 if seg else 1)]
+        print(f"[trace] segmented={seg} spans ms {spans}", flush=True)
+        assert all(sp >= 0.0 for sp in spans) and sum(spans) > 0.0
