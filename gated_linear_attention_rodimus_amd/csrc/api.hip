@@ -146,6 +146,7 @@ const char *rodimus_status_string(rodimus_status s)
     case RODIMUS_ERR_UNSUPPORTED: return "unsupported shape, chunk or dtype";
     case RODIMUS_ERR_WORKSPACE: return "workspace missing or too small";
     case RODIMUS_ERR_HIP: return "HIP runtime error";
+    default: break;
     }
     return "unknown status";
 }

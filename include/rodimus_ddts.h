@@ -63,17 +63,25 @@ extern "C" {
 
 #define RODIMUS_ABI_VERSION 1
 
+/* The two enums carry sentinel members that make every int a valid value of
+ * their type: a caller's out-of-range code (e.g. a dtype of 7) then reaches
+ * the library's checks, which reject it, instead of being undefined in the
+ * C++ implementation.  The sentinels are not statuses or dtypes. */
 typedef enum {
     RODIMUS_OK = 0,
     RODIMUS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, overlap */
     RODIMUS_ERR_UNSUPPORTED = 2,   /* width, chunk or dtype outside the supported set */
     RODIMUS_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-    RODIMUS_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+    RODIMUS_ERR_HIP = 4,           /* a HIP launch or runtime call failed */
+    RODIMUS_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    RODIMUS_STATUS_RANGE_MAX_ = 2147483647
 } rodimus_status;
 
 typedef enum {
     RODIMUS_DTYPE_F32 = 0,
-    RODIMUS_DTYPE_BF16 = 1
+    RODIMUS_DTYPE_BF16 = 1,
+    RODIMUS_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    RODIMUS_DTYPE_RANGE_MAX_ = 2147483647
 } rodimus_dtype;
 
 /* ABI version of the loaded library (RODIMUS_ABI_VERSION). */

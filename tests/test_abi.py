@@ -37,6 +37,8 @@ def test_version_and_status_strings():
     for s in range(5):
         assert L.rodimus_status_string(s)
     assert L.rodimus_status_string(0) == b"ok"
+    assert L.rodimus_status_string(99) == b"unknown status"
+    assert L.rodimus_status_string(-1) == b"unknown status"
 
 
 def _chunk(B=1, T=128, H=2, dk=64, dv=128, chunk=0, segments=0, dtype=R.DTYPE_BF16,
