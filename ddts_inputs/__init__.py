@@ -273,3 +273,57 @@ def make_fused(name: str, conv_width: int = 4, rank: int = 16, sub: int = 0,
         draw(_CQ, (H, dk, W), 1.0 / math.sqrt(W)),
         draw(_CK, (H, dk, W), 1.0 / math.sqrt(W)),
         draw(_CV, (H, dv, W), 1.0 / math.sqrt(W)))
+
+
+# ---------------------------------------------------------------- SW-SKA inputs
+@dataclasses.dataclass(frozen=True)
+class SwskaWorkload:
+    name: str
+    wid: int
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    window: int
+    dtype: str
+
+
+SWSKA_WORKLOADS = {
+    # the sliding-window shared-key attention of a 1.6B-scale Rodimus+ layer:
+    # 4 sequences x 4096 tokens, 16 query/value heads of 128, one shared key
+    # of 128, a 512-token window
+    "swska_1p6b": SwskaWorkload("swska_1p6b", 6, 4, 4096, 16, 128, 128, 512, "bf16"),
+}
+
+
+@dataclasses.dataclass
+class SwskaInputs:
+    """q [B, T, H, dk], k [B, T, dk] (shared by the heads), v [B, T, H, dv],
+    all N(0, 1), in the storage encoding."""
+    wl: SwskaWorkload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+    def f32(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+
+    def torch(self, name: str, device="cuda"):
+        import torch
+        a = getattr(self, name)
+        t = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
+             else torch.from_numpy(a))
+        return t.to(device)
+
+
+def make_swska(name: str = "swska_1p6b", sub: int = 0, **overrides) -> SwskaInputs:
+    wl = dataclasses.replace(SWSKA_WORKLOADS[name], **overrides)
+    B, T, H = wl.B, wl.T, wl.H
+
+    def draw(tid, shape):
+        return _encode(_rng(wl.wid, tid, sub).standard_normal(shape, dtype=np.float32), wl.dtype)
+
+    return SwskaInputs(wl, draw(_Q, (B, T, H, wl.dk)), draw(_K, (B, T, wl.dk)),
+                       draw(_V, (B, T, H, wl.dv)))

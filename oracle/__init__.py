@@ -260,3 +260,35 @@ def decode_fused(q, k, v, g, tau, state, beta_hat=None, u=None, w=None, d=None, 
     if d is not None:
         o = o + _f64(d)[None] * _f64(v)
     return o, st
+
+
+# ---------------------------------------------------------------- SW-SKA
+# Rodimus+'s second token mixer: sliding-window attention whose keys are
+# shared by all heads (summary page, "Approach"; digest page, "Method",
+# Rodimus+ bullets; the rebuttal counts its projections as multi-head,
+# multi-query and output, so q and v have a head each and k one for all).
+# Readings: token t attends to the `window` most recent tokens s with
+# t - window < s <= t (itself included); scores are q . k scaled by
+# 1 / sqrt(dk) unless a scale is given; softmax over those tokens.
+
+
+def swska_fwd(q, k, v, window, scale=None):
+    """Sliding-window shared-key attention in fp64.
+
+    q [B, T, H, dk], k [B, T, dk] (one key per token, shared by the heads),
+    v [B, T, H, dv] -> o [B, T, H, dv]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    assert k.shape == (B, T, dk) and v.shape[:3] == (B, T, H) and window >= 1
+    sc = 1.0 / np.sqrt(dk) if scale is None else float(scale)
+    o = np.empty((B, T, H, dv))
+    for b in range(B):
+        for t in range(T):
+            s0 = max(0, t - window + 1)
+            z = (q[b, t] @ k[b, s0:t + 1].T) * sc                 # [H, L]
+            z -= z.max(axis=1, keepdims=True)
+            p = np.exp(z)
+            p /= p.sum(axis=1, keepdims=True)
+            o[b, t] = np.einsum("hl,lhd->hd", p, v[b, s0:t + 1])
+    return o
