@@ -54,6 +54,16 @@ def chunk_algorithmic(B, T, H, dk, dv, C, in_bytes=2, state_in=False, state_out=
     return by, fl
 
 
+def swska_algorithmic(B, T, H, dk, dv, window, in_bytes=2):
+    """Flops of the sliding-window shared-key attention (q . k and p v over
+    each token's window, min(t + 1, window) keys) and the bytes it must move
+    (q, v per token and head, the shared k per token, o fp32)."""
+    keys = sum(min(t + 1, window) for t in range(T))
+    fl = 2 * B * H * keys * (dk + dv)
+    by = B * T * (H * (dk + dv) * in_bytes + dk * in_bytes + H * dv * 4)
+    return by, fl
+
+
 def decode_algorithmic(N, H, dk, dv, in_bytes=2):
     by = 2 * N * H * dk * dv * 4 + N * H * (4 * dk + 2 * dv) * in_bytes + N * H * dv * 4
     return by, 5 * N * H * dk * dv
@@ -165,6 +175,8 @@ def main():
     ap.add_argument("--other-workloads", default="layer130m,layer1p6b",
                     help="comma-separated forward workloads timed after the main one "
                          "('none': skip)")
+    ap.add_argument("--swska-steps", type=int, default=20,
+                    help="timed calls of the sliding-window shared-key attention (0: skip)")
     ap.add_argument("--fused-steps", type=int, default=20,
                     help="timed calls of the 130M layer fed low-rank beta_hat factors (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -331,6 +343,29 @@ def main():
                  "algorithmic_GBps": round(fby / fus / 1e3, 1),
                  "frac_hbm": round(fby / fus / 1e3 / HBM_PEAK_GBPS, 4)}
         del fsets
+        torch.cuda.empty_cache()
+
+    # ---------------- SW-SKA on a 1.6B-scale Rodimus+ layer
+    swska = None
+    if args.swska_steps > 0:
+        sxw = D.make_swska("swska_1p6b")
+        w_ = sxw.wl
+        ssets = [[sxw.torch(n, dev) for n in ("q", "k", "v")] for _ in range(2)]
+        so = torch.empty(w_.B, w_.T, w_.H, w_.dv, device=dev)
+        sstep = lambda i: R.swska_fwd(*ssets[i % 2], w_.window, out=so)
+        warm(sstep, 0.025)
+        sus = timed(sstep, args.swska_steps, stream)
+        sby, sfl = swska_algorithmic(w_.B, w_.T, w_.H, w_.dk, w_.dv, w_.window)
+        swska = {"workload": f"swska_1p6b: B={w_.B} T={w_.T} H={w_.H} dk={w_.dk} dv={w_.dv} bf16, "
+                             f"one shared key, window {w_.window}, fp32 out",
+                 "us_per_call": round(sus, 2),
+                 "tokens_per_s": round(w_.B * w_.T / (sus * 1e-6), 1),
+                 "algorithmic_flops_per_call": sfl,
+                 "tflops": round(sfl / (sus * 1e-6) / 1e12, 1),
+                 "frac_mfma_bf16": round(sfl / (sus * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "algorithmic_bytes_per_call": sby,
+                 "frac_hbm": round(sby / sus / 1e3 / HBM_PEAK_GBPS, 4)}
+        del ssets, so
         torch.cuda.empty_cache()
 
     # ---------------- decode: back-to-back steps over resident states
@@ -503,7 +538,7 @@ def main():
                        "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
                        "rotating_input_sets": args.rotate, "parallelism": "single GPU"},
             "roofline": roofline, "cpu_baseline": cpu, "other_forward": others or None,
-            "fused": fused, "decode": decode, "backward": backward, "serving": serving,
+            "fused": fused, "swska": swska, "decode": decode, "backward": backward, "serving": serving,
             "parity": parity}
     print(json.dumps(line), flush=True)
 

@@ -23,7 +23,8 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "chunk_fwd_no_alloc", "chunk_bwd", "decode_step",
-           "decode_step_fused", "workspace_bytes", "fused_workspace_bytes", "trace_forward_events",
+           "decode_step_fused", "swska_fwd", "workspace_bytes", "fused_workspace_bytes",
+           "trace_forward_events",
            "bwd_workspace_bytes", "chunk_fwd_plan", "STATIC_SCRATCH_BYTES",
            "lib", "RodimusError", "LIB_PATH", "abi_version"]
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_ddts_decode_step_fused.restype = i
         L.rodimus_ddts_decode_step_fused.argtypes = ([i] * 5 + [vp] * 6 + [ctypes.POINTER(_Fused)]
                                                      + [vp] * 3)
+        L.rodimus_swska_fwd.restype = i
+        L.rodimus_swska_fwd.argtypes = [i] * 6 + [ctypes.c_float, i] + [vp] * 4 + [vp]
         L.rodimus_trace_forward_events.restype = i
         L.rodimus_trace_forward_events.argtypes = [vp, i]
         L.rodimus_ddts_decode_step.restype = i
@@ -390,6 +393,32 @@ def trace_forward_events(events):
         st = lib().rodimus_trace_forward_events(handles, 4)
     if st != OK:
         raise RodimusError(st, "rodimus_trace_forward_events")
+
+
+def swska_fwd(q, k, v, window, scale=0.0, out=None):
+    """Sliding-window shared-key attention (rodimus_swska_fwd): q [B, T, H, dk],
+    k [B, T, dk] (one key for all heads), v [B, T, H, dv], bf16, contiguous,
+    on one GPU; each token attends to the ``window`` most recent tokens
+    (itself included); scale 0 = 1/sqrt(dk).  Returns o fp32 [B, T, H, dv]."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("swska_fwd runs on the GPU only; inputs must be on a cuda device")
+    code = _dtype_code(q)
+    _check_tensor("q", q, (B, T, H, dk), q.dtype, dev)
+    _check_tensor("k", k, (B, T, dk), q.dtype, dev)
+    _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("out", out, (B, T, H, dv), torch.float32, dev)
+    st = lib().rodimus_swska_fwd(B, T, H, dk, dv, int(window), float(scale), code, _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(out), _stream(dev))
+    if st != OK:
+        raise RodimusError(st, "rodimus_swska_fwd")
+    return out
 
 
 def decode_step(q, k, v, g, tau, beta_hat, state, out=None):

@@ -6,6 +6,7 @@
 
 #include <stdint.h>
 
+#include <math.h>
 #include <mutex>
 
 using namespace rodimus;
@@ -559,6 +560,31 @@ rodimus_status rodimus_ddts_decode_step_fused(
     f.conv_w = fused->conv_width; f.cq = fused->conv_q; f.ck = fused->conv_k; f.cv = fused->conv_v;
     hipError_t e = launch_decode(N, H, dk, dv, in_dtype == RODIMUS_DTYPE_F32,
                                  TokenInputs{q, k, g, tau, v, beta_hat}, state, out, stream, &f);
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+rodimus_status rodimus_swska_fwd(int B, int T, int H, int dk, int dv, int window, float scale,
+                                 rodimus_dtype in_dtype, const void *q, const void *k,
+                                 const void *v, float *out, hipStream_t stream)
+{
+    if (B <= 0 || H <= 0 || T < 0 || window < 1) return RODIMUS_ERR_INVALID_ARG;
+    if (in_dtype != RODIMUS_DTYPE_BF16) return RODIMUS_ERR_UNSUPPORTED;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return RODIMUS_ERR_UNSUPPORTED;
+    if (!(scale >= 0.f) || scale > 3.0e38f) return RODIMUS_ERR_INVALID_ARG;   // NaN, negative, Inf
+    if ((long long)B * ((T + 63) / 64) * H > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    if ((long long)B * T > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    if (T == 0) return RODIMUS_OK;
+    const void *ins[3] = {q, k, v};
+    for (const void *p : ins)
+        if (!p || !aligned16(p)) return RODIMUS_ERR_INVALID_ARG;
+    if (!out || !aligned16(out)) return RODIMUS_ERR_INVALID_ARG;
+    const size_t ntok = (size_t)B * T;
+    const Span s_o = span(out, ntok * H * dv * sizeof(float));
+    if (overlap(s_o, span(q, ntok * H * dk * 2)) || overlap(s_o, span(k, ntok * dk * 2)) ||
+        overlap(s_o, span(v, ntok * H * dv * 2)))
+        return RODIMUS_ERR_INVALID_ARG;
+    const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)dk);
+    hipError_t e = launch_swska(B, T, H, dk, dv, window, sc, q, k, v, out, stream);
     return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
 }
 

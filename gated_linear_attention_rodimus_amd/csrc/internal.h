@@ -115,6 +115,11 @@ struct ChunkBwdLaunch {
     float *d_chunks;        // [B*H][ceil(T / chunk)][dk][dv] dL/dS leaving every chunk (written)
     float *dq, *dk_, *dg, *dtau, *dv_, *dbeta, *ds0;
 };
+// Sliding-window shared-key attention (bf16 inputs, fp32 out), dk, dv in {64, 128}.
+hipError_t launch_swska(int B, int T, int H, int dk, int dv, int window, float scale,
+                        const void *q, const void *k, const void *v, float *out,
+                        hipStream_t stream);
+
 size_t chunk_bwd_lds_bytes(int dk, int dv, bool f32_inputs);   // 0 if the shape is not instantiated
 int chunk_bwd_chunk(int dk);                   // tokens per chunk of the backward
 hipError_t launch_chunk_bwd(const ChunkBwdLaunch &L, hipStream_t stream);

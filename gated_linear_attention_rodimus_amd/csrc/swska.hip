@@ -1,0 +1,300 @@
+// swska.hip -- sliding-window attention with one key shared by all heads
+// (SW-SKA, Rodimus+'s second token mixer) on gfx950 MFMA.
+//
+// What it computes (summary page, "Approach"; digest page, "Method",
+// Rodimus+ bullets: sliding-window attention whose keys are shared across
+// heads; the rebuttal counts its projections as multi-head, multi-query and
+// output, so q and v have a head each and k one for all): per batch b, head h
+// and token t,
+//     o[b,t,h] = sum_{t-W < s <= t} softmax_s(scale * q[b,t,h] . k[b,s]) v[b,s,h]
+// with scale 1/sqrt(dk) by default.
+//
+// Workgroup: 4 waves, one (b, 64-query block, h); wave w owns queries
+// q0 + 16 w .. + 15.  Key tiles of 64 cover [q0 - W + 1, q0 + 63]; per tile,
+//  - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS as A operands,
+//    the wave's queries as B operands held in registers): the C-layout of S^T
+//    (lane = query column, 4 consecutive keys per lane) is directly the B
+//    operand of the next product, so the probabilities never go through LDS;
+//  - an online softmax in fp32 per query (running maximum and sum, the
+//    output rescaled when the maximum moves), exponentials as exp2;
+//  - O^T += V^T P^T, V^T read with the transposing LDS read, P split into two
+//    bf16 terms (hi + lo, ~16 bits) so the product keeps fp32-level accuracy.
+// The next tile's K and V rows are loaded into registers while the current
+// one is in use.  Block ids put the heads of one query block on one XCD, so
+// the shared key tile is read from HBM once and from that XCD's L2 by the
+// other heads.
+#include "internal.h"
+
+#include <math.h>
+
+namespace rodimus {
+namespace swska_detail {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QB = 64;        // queries per workgroup
+constexpr int KB = 64;        // keys per tile
+constexpr int NT = 256;       // threads per workgroup
+
+template <int DK, int DV>
+struct Cfg {
+    static constexpr int KS = DK + 8;     // K row stride in LDS (bf16)
+    static constexpr int VS = DV + 8;     // V row stride
+    static constexpr size_t k_bytes = (size_t)KB * KS * 2;
+    static constexpr size_t bytes = k_bytes + (size_t)KB * VS * 2;
+    static constexpr int KL = KB * DK / 8 / NT;   // 16-byte K loads per thread per tile
+    static constexpr int VL = KB * DV / 8 / NT;   // 16-byte V loads per thread per tile
+};
+
+struct Args {
+    int T, H, window;
+    float scale_log2;            // scale * log2(e)
+    const __bf16 *q, *k, *v;     // [B][T][H][dk], [B][T][dk], [B][T][H][dv]
+    float *out;                  // [B][T][H][dv]
+    int remap;                   // XCD-aware block order on/off
+};
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane m
+// passes the address of 4 consecutive 16-bit values (row m/4, columns
+// 4*(m%4)..+3 of a 4 x 16 block); lane i receives column i, rows 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(const_cast<__bf16 *>(p)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Two fp32 values split into hi and lo bf16 pairs (round to nearest even;
+// the residual x - hi is exact in fp32).
+__device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigned &lo) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 x = {x0, x1};
+    const bf2 h = __builtin_convertvector(x, bf2);
+    const f2 hf = __builtin_convertvector(h, f2);
+    const f2 r = x - hf;
+    hi = __builtin_bit_cast(unsigned, h);
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector(r, bf2));
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(NT) void swska_fwd_kernel(Args a)
+{
+    typedef Cfg<DK, DV> L;
+    constexpr int KSQ = DK / 32;                 // MFMA k-steps over dk
+    constexpr int NDV = DV / 16;                 // output tiles over dv
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __bf16 *sK = (__bf16 *)smem;
+    __bf16 *sV = (__bf16 *)(smem + L::k_bytes);
+
+    // ---- block -> (b, query block, head); consecutive ids (the heads of one
+    // query block) on one XCD
+    const int nqb = (a.T + QB - 1) / QB;
+    const int nblk = gridDim.x;
+    int id = blockIdx.x;
+    if (a.remap) id = (id % 8) * (nblk / 8) + id / 8;
+    const int h = id % a.H;
+    const int qb = (id / a.H) % nqb;
+    const int b = id / a.H / nqb;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lc = lane & 15, lg = lane >> 4;
+    const long long T = a.T, H = a.H;
+    const int q0 = qb * QB;
+    const int tq = q0 + 16 * wave + lc;          // this lane's query
+    const bool qvalid = tq < a.T;
+
+    // Q^T as B operands: column = query tq, k = dk {32 ks + 4 lg .. +3, 32 ks + 16 + 4 lg .. +3}
+    bf16x8 qB[KSQ];
+    {
+        const __bf16 *qp = a.q + (((long long)b * T + (qvalid ? tq : 0)) * H + h) * DK;
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+            bf16x4 lo = *(const bf16x4 *)(qp + 32 * ks + 4 * lg);
+            bf16x4 hi = *(const bf16x4 *)(qp + 32 * ks + 16 + 4 * lg);
+            if (!qvalid) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lo[e] = hi[e] = (__bf16)0.f;
+            }
+            qB[ks] = cat(lo, hi);
+        }
+    }
+
+    // keys of the block: [kstart, kend)
+    const int kstart = q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0;
+    const int kend = q0 + QB < a.T ? q0 + QB : a.T;
+    const __bf16 *kbase = a.k + (long long)b * T * DK;
+    const __bf16 *vbase = a.v + ((long long)b * T * H + h) * DV;
+
+    // a tile's K and V rows into registers (rows past kend: zero)
+    u32x4 rk[L::KL], rv[L::VL];
+    auto load_tile = [&](int kt0) {
+#pragma unroll
+        for (int j = 0; j < L::KL; ++j) {
+            const int c = tid + NT * j;                    // 16-byte piece
+            const int r = c / (DK / 8), col = (c % (DK / 8)) * 8;
+            rk[j] = kt0 + r < kend ? *(const u32x4 *)(kbase + (long long)(kt0 + r) * DK + col)
+                                   : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < L::VL; ++j) {
+            const int c = tid + NT * j;
+            const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+            rv[j] = kt0 + r < kend ? *(const u32x4 *)(vbase + (long long)(kt0 + r) * H * DV + col)
+                                   : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stage_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < L::KL; ++j) {
+            const int c = tid + NT * j;
+            const int r = c / (DK / 8), col = (c % (DK / 8)) * 8;
+            *(u32x4 *)(sK + r * L::KS + col) = rk[j];
+        }
+#pragma unroll
+        for (int j = 0; j < L::VL; ++j) {
+            const int c = tid + NT * j;
+            const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+            *(u32x4 *)(sV + r * L::VS + col) = rv[j];
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;                 // running maximum (log2 units) and sum
+    f32x4 o[NDV];
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (kstart < kend) load_tile(kstart);
+    for (int kt0 = kstart; kt0 < kend; kt0 += KB) {
+        __syncthreads();                          // the previous tile's reads are done
+        stage_tile();
+        __syncthreads();
+        if (kt0 + KB < kend) load_tile(kt0 + KB);
+
+        // ---- S^T = K Q^T for the tile's 4 key blocks of 16
+        f32x4 s[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const __bf16 *kr = sK + (16 * kt + lc) * L::KS;
+#pragma unroll
+            for (int ks = 0; ks < KSQ; ++ks) {
+                const bf16x8 A = cat(*(const bf16x4 *)(kr + 32 * ks + 4 * lg),
+                                     *(const bf16x4 *)(kr + 32 * ks + 16 + 4 * lg));
+                s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qB[ks], s[kt], 0, 0, 0);
+            }
+        }
+        // ---- window mask, scale (log2 units), online softmax for query tq
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kt0 + 16 * kt + 4 * lg + r;
+                const bool ok = qvalid && key < kend && key <= tq && key > tq - a.window;
+                const float x = ok ? s[kt][r] * a.scale_log2 : -INFINITY;
+                s[kt][r] = x;
+                mloc = fmaxf(mloc, x);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float mnew = fmaxf(m, mloc);
+        const bool any = mnew != -INFINITY;
+        const float corr = (any && m != -INFINITY) ? __builtin_amdgcn_exp2f(m - mnew) : (any ? 0.f : 1.f);
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = any ? __builtin_amdgcn_exp2f(s[kt][r] - mnew) : 0.f;
+                s[kt][r] = p;
+                psum += p;
+            }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l = l * corr + psum;
+        m = mnew;
+#pragma unroll
+        for (int dt = 0; dt < NDV; ++dt) o[dt] *= corr;
+
+        // ---- O^T += V^T P^T over the tile's two 32-key k-steps
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            unsigned h01, l01, h23, l23, h45, l45, h67, l67;
+            split2(s[2 * k2][0], s[2 * k2][1], h01, l01);
+            split2(s[2 * k2][2], s[2 * k2][3], h23, l23);
+            split2(s[2 * k2 + 1][0], s[2 * k2 + 1][1], h45, l45);
+            split2(s[2 * k2 + 1][2], s[2 * k2 + 1][3], h67, l67);
+            const bf16x8 pH = __builtin_bit_cast(bf16x8, u32x4{h01, h23, h45, h67});
+            const bf16x8 pL = __builtin_bit_cast(bf16x8, u32x4{l01, l23, l45, l67});
+            const int row = 32 * k2 + 4 * lg + (lc >> 2), col = 4 * (lc & 3);
+#pragma unroll
+            for (int dt = 0; dt < NDV; ++dt) {
+                const bf16x4 vlo = lds_read_tr(sV + row * L::VS + 16 * dt + col);
+                const bf16x4 vhi = lds_read_tr(sV + (row + 16) * L::VS + 16 * dt + col);
+                const bf16x8 A = cat(vlo, vhi);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pL, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pH, o[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- o / l: lane holds dv 16 dt + 4 lg .. +3 of query tq
+    if (qvalid) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float *op = a.out + (((long long)b * T + tq) * H + h) * DV;
+#pragma unroll
+        for (int dt = 0; dt < NDV; ++dt)
+            __builtin_nontemporal_store(o[dt] * inv, (f32x4 *)(op + 16 * dt + 4 * lg));
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_typed(int B, int T, int H, int window, float scale, const void *q,
+                        const void *k, const void *v, float *out, hipStream_t stream)
+{
+    typedef Cfg<DK, DV> L;
+    static std::atomic<bool> lds_set[kMaxDevices];
+    hipError_t e = set_lds_limit_once((const void *)swska_fwd_kernel<DK, DV>, L::bytes, lds_set);
+    if (e != hipSuccess) return e;
+    Args a;
+    a.T = T; a.H = H; a.window = window;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.q = (const __bf16 *)q; a.k = (const __bf16 *)k; a.v = (const __bf16 *)v;
+    a.out = out;
+    const long long blocks = (long long)B * ((T + QB - 1) / QB) * H;
+    a.remap = blocks % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL((swska_fwd_kernel<DK, DV>), dim3((unsigned)blocks), dim3(NT), L::bytes,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace swska_detail
+
+hipError_t launch_swska(int B, int T, int H, int dk, int dv, int window, float scale,
+                        const void *q, const void *k, const void *v, float *out,
+                        hipStream_t stream)
+{
+    using namespace swska_detail;
+#define RODIMUS_SWSKA_DV(DK)                                                                   \
+    switch (dv) {                                                                              \
+    case 64: return launch_typed<DK, 64>(B, T, H, window, scale, q, k, v, out, stream);        \
+    case 128: return launch_typed<DK, 128>(B, T, H, window, scale, q, k, v, out, stream);      \
+    }                                                                                          \
+    break;
+    switch (dk) {
+    case 64: RODIMUS_SWSKA_DV(64)
+    case 128: RODIMUS_SWSKA_DV(128)
+    }
+#undef RODIMUS_SWSKA_DV
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rodimus

@@ -295,6 +295,32 @@ rodimus_status rodimus_ddts_decode_step_fused(
     float *state, float *out, hipStream_t stream);
 
 /*
+ * Sliding-window attention with one key shared by all heads (SW-SKA, the
+ * second token mixer of Rodimus+): the summary page ("Approach") and the
+ * digest page ("Method", Rodimus+ bullets) describe sliding-window attention
+ * whose keys are shared across heads; the rebuttal (answer on the Rodimus+
+ * parameter count) splits its projections into multi-head, multi-query and
+ * output ones, so q and v have a head each and k one for all.  Per batch b,
+ * head h and token t:
+ *     o[b,t,h] = sum over t - window < s <= t of softmax_s(scale q[b,t,h] . k[b,s]) v[b,s,h]
+ *
+ *   B, T, H       sizes; B, H >= 1, T >= 0 (T == 0 does nothing).
+ *   dk, dv        64 or 128.
+ *   window        tokens each query attends to, itself included (>= 1).
+ *   scale         score scale; 0 = 1 / sqrt(dk).  Negative, Inf or NaN:
+ *                 RODIMUS_ERR_INVALID_ARG.
+ *   in_dtype      RODIMUS_DTYPE_BF16 (others: RODIMUS_ERR_UNSUPPORTED).
+ *   q             [B, T, H, dk]; k [B, T, dk] (shared); v [B, T, H, dv].
+ *   out           [B, T, H, dv] fp32; must not overlap the inputs.
+ * Precision: q . k on bf16 MFMA with fp32 accumulation (exact products), the
+ * softmax in fp32, the probabilities split into two bf16 terms for the
+ * product with v.  No workspace.
+ */
+rodimus_status rodimus_swska_fwd(int B, int T, int H, int dk, int dv, int window, float scale,
+                                 rodimus_dtype in_dtype, const void *q, const void *k,
+                                 const void *v, float *out, hipStream_t stream);
+
+/*
  * Backward of rodimus_ddts_chunk_fwd (the training pass's other half): the
  * gradients of a loss L with respect to every input of the forward, given
  * dL/d out and optionally dL/d final_state.  The pages state that training

@@ -354,3 +354,33 @@ def test_trace_events_argument_checks():
     assert L.rodimus_trace_forward_events(arr, 3) == R.ERR_INVALID_ARG
     assert L.rodimus_trace_forward_events(arr, 4) == R.OK
     assert L.rodimus_trace_forward_events(None, 0) == R.OK
+
+
+def test_swska_argument_checks():
+    """SW-SKA rejects bad sizes, dtypes, widths, scales, pointers and overlaps
+    on the host (no GPU needed)."""
+    L = R.lib()
+    vp = ctypes.c_void_p
+    B, T, H, dk, dv = 2, 100, 4, 128, 128
+    q, k, v, o = BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 192 * MB
+
+    def call(B=B, T=T, H=H, dk=dk, dv=dv, window=16, scale=0.0, dt=R.DTYPE_BF16,
+             q=q, k=k, v=v, o=o):
+        return L.rodimus_swska_fwd(B, T, H, dk, dv, window, scale, dt,
+                                   vp(q) if q else None, vp(k) if k else None,
+                                   vp(v) if v else None, vp(o) if o else None, None)
+
+    assert call(window=0) == R.ERR_INVALID_ARG
+    assert call(B=0) == R.ERR_INVALID_ARG
+    assert call(T=-1) == R.ERR_INVALID_ARG
+    assert call(dt=R.DTYPE_F32) == R.ERR_UNSUPPORTED
+    assert call(dk=32) == R.ERR_UNSUPPORTED
+    assert call(dv=16) == R.ERR_UNSUPPORTED
+    assert call(scale=-1.0) == R.ERR_INVALID_ARG
+    assert call(scale=float("nan")) == R.ERR_INVALID_ARG
+    assert call(scale=float("inf")) == R.ERR_INVALID_ARG
+    assert call(q=0) == R.ERR_INVALID_ARG
+    assert call(v=v + 2) == R.ERR_INVALID_ARG           # misaligned
+    assert call(o=q) == R.ERR_INVALID_ARG               # out over q
+    assert call(o=k + 1024) == R.ERR_INVALID_ARG        # out over k
+    assert call(T=0) == R.OK                             # nothing to do, nothing launched

@@ -60,3 +60,10 @@ def test_pass_traffic_record_is_consistent():
     got = bench.kernel_traffic("output")
     assert got == (rec["passes"]["output"]["hbm_bytes_per_launch"]
                    if sha == rec["kernel_source_sha256"] else None)
+
+
+def test_swska_work_model():
+    # T = 3, window 2: keys per token 1, 2, 2 -> 5 (b, h) key visits
+    by, fl = bench.swska_algorithmic(1, 3, 2, 4, 8, 2)
+    assert fl == 2 * 2 * 5 * (4 + 8)
+    assert by == 3 * (2 * (4 + 8) * 2 + 4 * 2 + 2 * 8 * 4)
