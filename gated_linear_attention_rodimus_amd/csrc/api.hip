@@ -54,9 +54,7 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     for (int ci = 0; ci < 3 && !found; ++ci) {
         const int C = chunks_try[ci];
         if (chunk != 0 && C > chunk) continue;
-        // the fused kernels on fp32 inputs keep a load per ShortConv tap in
-        // registers: 16-token chunks, where they fit without spilling
-        if (fused && f32 && C > 16) continue;
+        // shapes that are not compiled report 0 bytes
         const size_t lds = chunk_lds_bytes(dk, dv < 64 ? dv : 64, C, f32, fused);
         if (lds == 0 || lds > kLdsLimit) continue;
         P->C = C;

@@ -150,9 +150,10 @@ template <int DK, int JT, int NS_>
 struct SweepCfg {
     static constexpr int NS = NS_;
     static constexpr int C = ChunkOf<DK>::C;
-    // 4 producer waves; 8 for fp32 inputs at dk = 128, whose two register
-    // sets of pair loads would not fit beside 8 state waves
-    static constexpr int NP = DK == 128 && NS == 3 ? 8 : 4;
+    // 4 producer waves; 8 at dk = 128, where two register sets of pair loads
+    // of 4-wave producers would not fit the registers that a 12-wave
+    // workgroup leaves each wave (170) and spill
+    static constexpr int NP = DK == 128 ? 8 : 4;
     static constexpr int NRB = DK / 16, NW = NP + NRB, NT = 64 * NW;
     static constexpr int PP = DK / 2;                          // dk column pairs
     static constexpr int GW = 64 / PP;                         // token groups per producer wave

@@ -314,11 +314,13 @@ struct Cfg {
     static constexpr size_t out_off = stg_off + (NS == 2 ? (size_t)NJ * stg_wave : 0);
     static constexpr size_t bytes = out_off + (OUT ? (size_t)C * OS * 4 : 0);
     // workgroups per CU the kernel is compiled for: two for bf16 inputs at
-    // dk <= 64 in the transfer mode, and in the output mode at C <= 32, where
-    // two fit the CU's LDS and four waves per SIMD leave each wave enough
-    // registers (128) without spilling; one otherwise
+    // dk <= 64 and C <= 32, and in the transfer mode also at C = 64 on tiles
+    // narrower than 64 x 64, where two fit the CU's LDS and the waves per SIMD
+    // that brings leave each wave enough registers (128) without spilling;
+    // one otherwise
     static constexpr int per_cu =
-        ((!OUT || C <= 32) && NS == 2 && 2 * bytes <= 160 * 1024 && DK <= 64 && !FU_) ? 2 : 1;
+        ((C <= 32 || (!OUT && (DK < 64 || DVT < 64))) && NS == 2 && 2 * bytes <= 160 * 1024 &&
+         DK <= 64 && !FU_) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
@@ -1179,13 +1181,23 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Shapes whose output-mode layout exceeds the CU's LDS (dk = 128 at C = 64)
-// are never planned; they are not instantiated either.
+// The tile shapes that are compiled (the size queries report 0 LDS bytes for
+// the others, so they are never planned): the output-mode layout fits the
+// CU's LDS, and the kernel fits its registers without spilling, which rules
+// out 64-token chunks at dk = 128 and, with the fused steps on fp32 inputs
+// (a load per ShortConv tap kept in registers), chunks beyond 16 tokens.
+template <int DK, int DVT, int C, int NS, bool FU>
+constexpr bool compiled_shape()
+{
+    return Cfg<DK, DVT, C, NS, true, FU>::bytes <= 160 * 1024 && !(DK == 128 && C == 64) &&
+           !(FU && NS == 3 && C > 16);
+}
+
 template <int DK, int DVT, int C, typename TIn, bool FU>
 hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
-    if constexpr (Cfg<DK, DVT, C, NS, true, FU>::bytes > 160 * 1024) {
+    if constexpr (!compiled_shape<DK, DVT, C, NS, FU>()) {
         return hipErrorInvalidValue;
     } else {
         return Lc.mode == 0 ? launch_mode<DK, DVT, C, TIn, true, FU>(Lc, stream)
@@ -1197,8 +1209,10 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 // fused steps (XF), and defines its size queries and launcher.
 #define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC, XF)                                        \
     if (dvt == XV && C == XC)                                                         \
-        return f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true, XF>::bytes                \
-                   : chunk_detail::Cfg<XK, XV, XC, 2, true, XF>::bytes;
+        return f32 ? (chunk_detail::compiled_shape<XK, XV, XC, 3, XF>()               \
+                          ? chunk_detail::Cfg<XK, XV, XC, 3, true, XF>::bytes : 0)    \
+                   : (chunk_detail::compiled_shape<XK, XV, XC, 2, XF>()               \
+                          ? chunk_detail::Cfg<XK, XV, XC, 2, true, XF>::bytes : 0);
 #define RODIMUS_CHUNK_CASE_PCU(XK, XV, XC, XF)                                        \
     if (dvt == XV && C == XC)                                                         \
         return outputs ? (f32 ? chunk_detail::Cfg<XK, XV, XC, 3, true, XF>::per_cu    \

@@ -119,7 +119,9 @@ def test_workspace_bytes_plan():
     # workgroups) and 3 transfers; fp32 inputs: 2 segments of 64-token chunks,
     # the first one's transfer cut in 2.  The larger need, 4 slots per head:
     assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 4 * (64 * 128 + 64) * 4
-    assert R.workspace_bytes(4, 4096, 16, 64, 128, 0, 2) == 4 * 16 * 4 * (64 * 128 + 64) * 4
+    # two segments asked for: 64-token chunks, the first segment's transfer
+    # cut in 2 (bf16 and fp32 alike), 2 slots per head
+    assert R.workspace_bytes(4, 4096, 16, 64, 128, 0, 2) == 4 * 16 * 2 * (64 * 128 + 64) * 4
     # long sequence, few heads: segmented
     ws = R.workspace_bytes(1, 65536, 16, 64, 128)
     assert ws > 0 and ws % (16 * (64 * 128 + 64) * 4) == 0
@@ -257,9 +259,13 @@ def test_plan_segmented_fp32_keeps_long_chunks():
 
 def test_plan_explicit_segments_and_chunk():
     # an explicit segment count keeps the longest chunk that fits; with 32
-    # chunks per segment the bf16 transfers (two per CU) are cut in 4
+    # chunks per segment the transfers (64 x 64 tiles of 64-token chunks: one
+    # per CU) are cut in 2
     p = _plan(4, 4096, 16, 64, 128, 0, 2)
-    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (64, 2, 4)
+    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (64, 2, 2)
+    # narrower dv tiles run two transfers per CU: cut in 4
+    p = _plan(4, 4096, 16, 64, 32, 0, 2)
+    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 32, 2, 4)
     # segments = 1 forces one sweep; the chunk request is an upper bound
     assert _plan(1, 65536, 16, 64, 128, 0, 1)["segments"] == 1
     assert _plan(8, 2048, 12, 64, 128, 16)["chunk"] == 16
