@@ -43,8 +43,10 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo 
 //    gate work is shared by as many columns as possible);
 //  - segments (when the caller passes 0): one sweep while the (b, h, tile)
 //    units fill more than half the CUs, else pieces of >= 8 chunks, as many
-//    as run at once, with 32-token chunks where those kernels hold two
-//    workgroups per CU;
+//    as run at once, on the whole-head 128-column tile where it is compiled
+//    (the gate work then done once per head; measured: long prefill 584 ->
+//    505 us, 1.6B layer 143 -> 135 us), otherwise with 32-token chunks where
+//    those kernels hold two workgroups per CU;
 //  - transfer pieces per segment: below.
 bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, bool f32,
                ChunkPlan *P, bool fused = false)
@@ -62,11 +64,31 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     }
     if (!found) return false;
     const long long heads = (long long)B * H;
-    const int dvt = dv < 64 ? dv : 64;
-    const long long units = heads * (dv / dvt);
+    int dvt = dv < 64 ? dv : 64;
+    long long units = heads * (dv / dvt);
     int seg = segments;
     if (seg == 0) {
         seg = 1;
+        // few units and long sequences: the whole-head tile at the longest
+        // chunk it has, when segments of >= 8 chunks, as many as run at once,
+        // fill the CUs
+        if (units <= kTargetBlocks / 2 && dv == 128) {
+            for (int ci = 0; ci < 3; ++ci) {
+                const int C = chunks_try[ci];
+                if (chunk != 0 && C > chunk) continue;
+                const size_t lds = chunk_lds_bytes(dk, 128, C, f32, fused);
+                if (lds == 0 || lds > kLdsLimit) continue;
+                const long long nch = T > 0 ? (T + C - 1) / C : 0;
+                const long long want = (long long)kTargetBlocks * chunk_per_cu(dk, 128, C, f32, true, fused) / heads;
+                if (want >= 2 && nch / 8 >= want) {
+                    P->C = C;
+                    dvt = 128;
+                    units = heads;
+                    seg = (int)want;
+                }
+                break;
+            }
+        }
         // one sweep per (b, h, dv tile) while that fills more than half the
         // CUs; at half or fewer, split the sequences into segments of at least
         // 8 chunks, as many as run at once.  Chunks of 32 tokens are taken
@@ -74,7 +96,7 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
         // segments; measured: long prefill, 16 heads x 2 tiles, 16 segments
         // of C = 32 584 us against 8 of C = 64 630 us; 1.6B layer, 64 heads x
         // 2 tiles, 4 of C = 32 142 us against 2 of C = 64 151 us)
-        if (units <= kTargetBlocks / 2) {
+        if (dvt != 128 && units <= kTargetBlocks / 2) {
             int Cs = P->C;
             if (P->C > 32 && chunk_per_cu(dk, dvt, 32, f32, true, fused) == 2 &&
                 chunk_lds_bytes(dk, dvt, 32, f32, fused) != 0)

@@ -317,10 +317,10 @@ struct Cfg {
     // dk <= 64 and C <= 32, and in the transfer mode also at C = 64 on tiles
     // narrower than 64 x 64, where two fit the CU's LDS and the waves per SIMD
     // that brings leave each wave enough registers (128) without spilling;
-    // one otherwise
+    // one otherwise, and always one for the 12-wave 128-column tile
     static constexpr int per_cu =
         ((C <= 32 || (!OUT && (DK < 64 || DVT < 64))) && NS == 2 && 2 * bytes <= 160 * 1024 &&
-         DK <= 64 && !FU_) ? 2 : 1;
+         DK <= 64 && !FU_ && NW <= 8) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
@@ -419,7 +419,9 @@ void chunk_fwd_kernel(Args a)
     // in interleaved groups.
     auto score_tiles = [&](int wi, int cb) {
         constexpr int TPW = (NA + NP - 1) / NP;            // tiles per wave
-        constexpr int G = TPW < 4 ? TPW : 4;               // interleave group
+        // interleave group; one tile at a time in the 12-wave 128-column tile,
+        // whose waves have 168 registers each
+        constexpr int G = L::NW > 8 ? 1 : TPW < 4 ? TPW : 4;
         const __bf16 *qb = bQ(cb), *kb = bK(cb);
 #pragma unroll
         for (int j0 = 0; j0 < TPW; j0 += G) {
@@ -1185,12 +1187,15 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 // the others, so they are never planned): the output-mode layout fits the
 // CU's LDS, and the kernel fits its registers without spilling, which rules
 // out 64-token chunks at dk = 128 and, with the fused steps on fp32 inputs
-// (a load per ShortConv tap kept in registers), chunks beyond 16 tokens.
+// (a load per ShortConv tap kept in registers), chunks beyond 16 tokens.  The
+// 128-column tile (a whole head of dv = 128: 4 producer and 8 consumer waves,
+// the gates' preparation done once per head) is compiled for bf16 inputs
+// without the fused steps, dk <= 64 and chunks of 32 or 64 tokens.
 template <int DK, int DVT, int C, int NS, bool FU>
 constexpr bool compiled_shape()
 {
     return Cfg<DK, DVT, C, NS, true, FU>::bytes <= 160 * 1024 && !(DK == 128 && C == 64) &&
-           !(FU && NS == 3 && C > 16);
+           !(FU && NS == 3 && C > 16) && (DVT < 128 || (NS == 2 && !FU && DK <= 64 && C >= 32));
 }
 
 template <int DK, int DVT, int C, typename TIn, bool FU>
@@ -1226,7 +1231,8 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 #define RODIMUS_CHUNK_SHAPES(X, XK, XF)                                               \
     X(XK, 16, 16, XF) X(XK, 16, 32, XF) X(XK, 16, 64, XF)                             \
     X(XK, 32, 16, XF) X(XK, 32, 32, XF) X(XK, 32, 64, XF)                             \
-    X(XK, 64, 16, XF) X(XK, 64, 32, XF) X(XK, 64, 64, XF)
+    X(XK, 64, 16, XF) X(XK, 64, 32, XF) X(XK, 64, 64, XF)                             \
+    X(XK, 128, 32, XF) X(XK, 128, 64, XF)
 #define RODIMUS_DEFINE_CHUNK(XK, XF, NAME)                                            \
     size_t chunk_lds_bytes_##NAME(int dvt, int C, bool f32)                           \
     {                                                                                 \

@@ -114,10 +114,10 @@ def test_chunk_workspace_required_for_segments():
 def test_workspace_bytes_plan():
     # one sweep when the (b, h, dv tile) units fill more than half the CUs: no workspace
     assert R.workspace_bytes(8, 2048, 12, 64, 128) == 0
-    # 64 heads x 2 dv tiles = half the CUs: segmented.  bf16 inputs: chunks of
-    # 32 tokens, whose kernels hold two workgroups per CU, so 4 segments (512
-    # workgroups) and 3 transfers; fp32 inputs: 2 segments of 64-token chunks,
-    # the first one's transfer cut in 2.  The larger need, 4 slots per head:
+    # 64 heads x 2 dv tiles = half the CUs: segmented.  bf16 inputs: the
+    # whole-head tile, 4 segments (256 workgroups) and 3 transfers; fp32
+    # inputs: 2 segments of 64-token chunks, the first one's transfer cut in
+    # 2.  The larger need, 4 slots per head:
     assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 4 * (64 * 128 + 64) * 4
     # two segments asked for: 64-token chunks, the first segment's transfer
     # cut in 2 (bf16 and fp32 alike), 2 slots per head
@@ -235,18 +235,26 @@ def test_plan_one_sweep_when_units_fill_the_gpu():
     assert _plan(8, 2048, 12, 64, 128, dtype="f32")["segments"] == 1
 
 
-def test_plan_segmented_bf16_takes_short_chunks():
-    # 1.6B layer: 64 heads x 2 tiles = 128 units, half the CUs.  bf16: 32-token
-    # chunks (two workgroups per CU), 512 / 128 = 4 segments, 3 transfers
+def test_plan_segmented_bf16_takes_whole_heads_or_short_chunks():
+    # 1.6B layer: 64 heads x 2 tiles = 128 units, half the CUs: segmented.
+    # bf16, dv = 128, sequences long enough: the whole-head tile (one
+    # workgroup per CU), 256 / 64 = 4 segments of 64-token chunks, 3 transfers
     p = _plan(4, 4096, 16, 64, 128)
-    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (32, 4, 1)
+    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 4, 1)
     assert p["workspace_bytes"] == 4 * 16 * 4 * (64 * 128 + 64) * 4
-    # long prefill: 16 heads x 2 tiles = 32 units -> 16 segments of 128 chunks
+    # long prefill: 16 heads -> 16 segments of 64 chunks
     p = _plan(1, 65536, 16, 64, 128)
-    assert (p["chunk"], p["segments"], p["transfer_pieces"]) == (32, 16, 1)
-    # the segment count is capped at one per 8 chunks
+    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 16, 1)
+    # too short for whole-head segments that fill the CUs: 64-column tiles,
+    # 32-token chunks (two workgroups per CU), the segment count capped at
+    # one per 8 chunks
     p = _plan(1, 1024, 2, 64, 128)
-    assert (p["chunk"], p["segments"]) == (32, 4)
+    assert (p["chunk"], p["dv_tile"], p["segments"]) == (32, 64, 4)
+    # no whole-head tile for fp32 inputs or dv < 128
+    assert _plan(1, 65536, 16, 64, 128, dtype="f32")["dv_tile"] == 64
+    assert _plan(1, 65536, 16, 64, 64)["dv_tile"] == 64
+    # nor at dk = 128
+    assert _plan(1, 65536, 16, 128, 128)["dv_tile"] == 64
 
 
 def test_plan_segmented_fp32_keeps_long_chunks():

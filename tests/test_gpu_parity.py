@@ -92,6 +92,17 @@ def test_layer1p6b_full_with_final_state(R, dev):
     check_full(R, x, dev, label="layer1p6b B4 T4096 H16 64x128 bf16 + S_T")
 
 
+@pytest.mark.parametrize("dk", [16, 32, 64])
+def test_whole_head_tile_segmented(R, dev, dk):
+    # 16 heads of dv = 128 over 8,229 tokens (ragged against 64-token chunks):
+    # the planner takes the whole-head 128-column tile, 15 segments, with an
+    # initial state and S_T
+    x = D.make("long_prefill", B=1, T=8192 + 37, H=16, dk=dk)
+    p = R.chunk_fwd_plan(1, x.wl.T, 16, dk, 128)
+    assert p["dv_tile"] == 128 and p["segments"] > 1, p
+    check_full(R, x, dev, s0=x.initial_state, label=f"whole-head dk {dk} {p}")
+
+
 @pytest.mark.timeout(600)
 def test_long_prefill_full(R, dev):
     x = D.make("long_prefill")
