@@ -52,6 +52,7 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
                ChunkPlan *P, bool fused = false)
 {
     const int chunks_try[3] = {64, 32, 16};
+    P->Ct = 0;
     bool found = false;
     for (int ci = 0; ci < 3 && !found; ++ci) {
         const int C = chunks_try[ci];
@@ -85,6 +86,12 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
                     dvt = 128;
                     units = heads;
                     seg = (int)want;
+                    // transfers in half-length chunks where that kernel holds
+                    // two workgroups per CU (measured: long prefill, transfer
+                    // pass 177 -> 160 us)
+                    if (C == 64 && chunk_per_cu(dk, 128, 32, f32, false, fused) == 2 &&
+                        chunk_lds_bytes(dk, 128, 32, f32, fused) != 0)
+                        P->Ct = 32;
                 }
                 break;
             }
@@ -121,17 +128,18 @@ bool make_plan(int B, int T, int H, int dk, int dv, int chunk, int segments, boo
     // drop empty trailing segments
     if (P->chunks_per_seg > 0) seg = (P->n_chunks + P->chunks_per_seg - 1) / P->chunks_per_seg;
     P->segments = seg;
+    if (P->Ct == 0 || seg == 1) P->Ct = P->C;
     // the transfers cover the segments before the last (the output pass of
     // the last one writes S_T from its true incoming state); each is cut into
     // 2 pieces where they all still run at once (measured: 1.6B layer, 64
     // heads x 2 tiles x 2 segments of C = 64, 180 -> 153 us), and into 4
     // pieces of at least 8 chunks where the CUs hold that many transfer
     // workgroups
-    const long long xfer_cap = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, P->C, f32, false, fused);
+    const long long xfer_cap = (long long)kTargetBlocks * chunk_per_cu(dk, dvt, P->Ct, f32, false, fused);
+    const int cps_t = P->chunks_per_seg * (P->C / P->Ct);             // transfer chunks per segment
     P->tr_per_seg = 1;
-    if (seg > 1 && P->chunks_per_seg % 2 == 0 && units * (seg - 1) * 2 <= xfer_cap) P->tr_per_seg = 2;
-    if (seg > 1 && P->chunks_per_seg % 4 == 0 && P->chunks_per_seg / 4 >= 8 &&
-        units * (seg - 1) * 4 <= xfer_cap)
+    if (seg > 1 && cps_t % 2 == 0 && units * (seg - 1) * 2 <= xfer_cap) P->tr_per_seg = 2;
+    if (seg > 1 && cps_t % 4 == 0 && cps_t / 4 >= 8 && units * (seg - 1) * 4 <= xfer_cap)
         P->tr_per_seg = 4;
     const int tr = (seg - 1) * P->tr_per_seg;
     P->ws_slots = seg > tr ? seg : tr;
@@ -375,7 +383,8 @@ rodimus_status chunk_fwd_launch(
     const int n_seg = P.segments, per = P.tr_per_seg, slots = P.ws_slots;
     float *ws_ds = (float *)workspace;                                // [BH][slots][dk][dv]
     float *ws_gam = ws_ds + (size_t)B * H * slots * dk * dv;          // [BH][slots][dk]
-    Lc.n_seg = (n_seg - 1) * per; Lc.chunks_per_seg = P.chunks_per_seg / per; Lc.mode = 1;
+    Lc.n_seg = (n_seg - 1) * per; Lc.mode = 1;
+    Lc.C = P.Ct; Lc.chunks_per_seg = P.chunks_per_seg * (P.C / P.Ct) / per;
     Lc.s_in = nullptr; Lc.s_in_bh_stride = 0; Lc.s_in_seg_stride = 0;
     Lc.out = nullptr;
     Lc.s_out = ws_ds; Lc.s_out_bh_stride = (long long)slots * sz; Lc.s_out_seg_stride = sz;
@@ -388,7 +397,7 @@ rodimus_status chunk_fwd_launch(
     e = launch_segment_combine(B * H, n_seg, per, slots, dk, dv, initial_state, ws_ds, ws_gam, stream);
     if (e == hipSuccess) e = trace(2, stream);
     if (e != hipSuccess) return RODIMUS_ERR_HIP;
-    Lc.n_seg = n_seg; Lc.chunks_per_seg = P.chunks_per_seg; Lc.mode = 0;
+    Lc.n_seg = n_seg; Lc.C = P.C; Lc.chunks_per_seg = P.chunks_per_seg; Lc.mode = 0;
     Lc.s_in = ws_ds; Lc.s_in_bh_stride = (long long)slots * sz; Lc.s_in_seg_stride = sz;
     Lc.out = out;
     Lc.s_out = final_state; Lc.s_out_bh_stride = sz; Lc.s_out_seg_stride = 0;

@@ -320,7 +320,7 @@ struct Cfg {
     // one otherwise, and always one for the 12-wave 128-column tile
     static constexpr int per_cu =
         ((C <= 32 || (!OUT && (DK < 64 || DVT < 64))) && NS == 2 && 2 * bytes <= 160 * 1024 &&
-         DK <= 64 && !FU_ && NW <= 8) ? 2 : 1;
+         DK <= 64 && !FU_ && (NW <= 8 || (!OUT && C <= 32))) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");

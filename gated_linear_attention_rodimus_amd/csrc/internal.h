@@ -36,6 +36,7 @@ struct TokenInputs {
 // How one chunk-forward call is executed.
 struct ChunkPlan {
     int C;          // tokens per chunk
+    int Ct;         // tokens per chunk of the segment transfers (C, or C / 2)
     int DVT;        // dv columns per workgroup
     int segments;   // pieces per (b, h) sequence run in parallel (1 = one sweep)
     int n_chunks;   // ceil(T / C)

@@ -193,8 +193,10 @@ rodimus_status rodimus_trace_forward_events(hipEvent_t *events, int count);
 
 /*
  * How rodimus_ddts_chunk_fwd_ex runs for these arguments and input dtype:
- *   chunk            tokens per chunk (16, 32 or 64);
- *   dv_tile          dv columns per workgroup;
+ *   chunk            tokens per chunk (16, 32 or 64) of the outputs (the
+ *                    segment transfers of a whole-head plan may run chunks
+ *                    of half that length over the same token ranges);
+ *   dv_tile          dv columns per workgroup (128: one workgroup per head);
  *   segments         pieces each (b, h) sequence is split into (1: one
  *                    sequential sweep);
  *   transfer_pieces  pieces each state transfer (one per segment but the

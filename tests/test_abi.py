@@ -115,10 +115,10 @@ def test_workspace_bytes_plan():
     # one sweep when the (b, h, dv tile) units fill more than half the CUs: no workspace
     assert R.workspace_bytes(8, 2048, 12, 64, 128) == 0
     # 64 heads x 2 dv tiles = half the CUs: segmented.  bf16 inputs: the
-    # whole-head tile, 4 segments (256 workgroups) and 3 transfers; fp32
-    # inputs: 2 segments of 64-token chunks, the first one's transfer cut in
-    # 2.  The larger need, 4 slots per head:
-    assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 4 * (64 * 128 + 64) * 4
+    # whole-head tile, 4 segments (256 workgroups), 3 transfers cut in 2 (6
+    # slots); fp32 inputs: 2 segments of 64-token chunks, the first one's
+    # transfer cut in 2.  The larger need, 6 slots per head:
+    assert R.workspace_bytes(4, 4096, 16, 64, 128) == 4 * 16 * 6 * (64 * 128 + 64) * 4
     # two segments asked for: 64-token chunks, the first segment's transfer
     # cut in 2 (bf16 and fp32 alike), 2 slots per head
     assert R.workspace_bytes(4, 4096, 16, 64, 128, 0, 2) == 4 * 16 * 2 * (64 * 128 + 64) * 4
@@ -238,13 +238,14 @@ def test_plan_one_sweep_when_units_fill_the_gpu():
 def test_plan_segmented_bf16_takes_whole_heads_or_short_chunks():
     # 1.6B layer: 64 heads x 2 tiles = 128 units, half the CUs: segmented.
     # bf16, dv = 128, sequences long enough: the whole-head tile (one
-    # workgroup per CU), 256 / 64 = 4 segments of 64-token chunks, 3 transfers
+    # workgroup per CU), 256 / 64 = 4 segments of 64-token chunks; the 3
+    # transfers run 32-token chunks at two workgroups per CU, each cut in 2
     p = _plan(4, 4096, 16, 64, 128)
-    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 4, 1)
-    assert p["workspace_bytes"] == 4 * 16 * 4 * (64 * 128 + 64) * 4
-    # long prefill: 16 heads -> 16 segments of 64 chunks
+    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 4, 2)
+    assert p["workspace_bytes"] == 4 * 16 * 6 * (64 * 128 + 64) * 4
+    # long prefill: 16 heads -> 16 segments of 64 chunks, 15 x 2 transfers
     p = _plan(1, 65536, 16, 64, 128)
-    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 16, 1)
+    assert (p["chunk"], p["dv_tile"], p["segments"], p["transfer_pieces"]) == (64, 128, 16, 2)
     # too short for whole-head segments that fill the CUs: 64-column tiles,
     # 32-token chunks (two workgroups per CU), the segment count capped at
     # one per 8 chunks
