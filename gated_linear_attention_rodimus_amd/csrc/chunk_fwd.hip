@@ -46,7 +46,10 @@ namespace {
 // S_in[0] = S0 (or 0); S_in[p + 1] = the transfers p * per .. p * per + per - 1
 // applied in order to S_in[p] (each: S <- diag(gam[j]) S + dS[j]); S_in[p] is
 // written to slot p, after every transfer in that slot has been read.  One
-// thread per state element, sequential over segments.
+// thread per state element, sequential over the transfers.  Up to 32
+// transfers are all loaded first (one memory latency for the whole chain);
+// beyond that, the next segment's transfers (per <= 4) are loaded while the
+// current ones are applied.
 __global__ __launch_bounds__(256) void segment_combine_kernel(
     int n_seg, int per, int slots, int dk, int dv, const float *__restrict__ s0,
     float *__restrict__ ds, const float *__restrict__ gam)
@@ -59,13 +62,46 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(
     float run = s0 ? s0[(size_t)bh * st + e] : 0.f;
     float *d = ds + (size_t)bh * slots * st + e;
     const float *gm = gam + (size_t)bh * slots * dk + i;
+    const int ntr = (n_seg - 1) * per;
+    if (ntr <= 32) {
+        float dd[32], gg[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            if (j < ntr) {
+                dd[j] = d[(size_t)j * st];
+                gg[j] = gm[(size_t)j * dk];
+            }
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            if (j < ntr) {
+                if ((j & (per - 1)) == 0) d[(size_t)(j / per) * st] = run;   // S_in of segment j / per
+                run = gg[j] * run + dd[j];
+            }
+        d[(size_t)(n_seg - 1) * st] = run;
+        return;
+    }
+    float nd[4] = {0.f, 0.f, 0.f, 0.f}, ng[4] = {0.f, 0.f, 0.f, 0.f};
+    auto fetch = [&](int p) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            if (f < per) {
+                const int j = p * per + f;
+                nd[f] = d[(size_t)j * st];
+                ng[f] = gm[(size_t)j * dk];
+            }
+    };
+    fetch(0);
     for (int p = 0; p < n_seg; ++p) {
         const float cur = run;
-        if (p + 1 < n_seg)
-            for (int f = 0; f < per; ++f) {
-                const int j = p * per + f;
-                run = gm[(size_t)j * dk] * run + d[(size_t)j * st];
-            }
+        if (p + 1 < n_seg) {
+            float cd[4], cg[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) { cd[f] = nd[f]; cg[f] = ng[f]; }
+            if (p + 2 < n_seg) fetch(p + 1);
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                if (f < per) run = cg[f] * run + cd[f];
+        }
         d[(size_t)p * st] = cur;
     }
 }
@@ -116,6 +152,8 @@ hipError_t launch_segment_combine(int BH, int n_seg, int per, int slots, int dk,
                                   const float *s0, float *ds_inout, const float *gam,
                                   hipStream_t stream)
 {
+    // the kernel holds 4 transfers per segment, and masks slots with per - 1
+    if (per != 1 && per != 2 && per != 4) return hipErrorInvalidValue;
     const int elems = dk * dv;
     dim3 grid((elems + 255) / 256, BH);
     hipLaunchKernelGGL(segment_combine_kernel, grid, dim3(256), 0, stream, n_seg, per, slots, dk,
