@@ -54,8 +54,12 @@ def test_pass_traffic_record_is_consistent():
         assert abs(hbm - p["hbm_bytes_per_launch"]) / hbm < 1e-4, name
         total += p["hbm_bytes_per_launch"]
     assert total == rec["call_hbm_bytes"]
+    # the output pass's own bytes: the call's, with the incoming state of each
+    # of the 16 segments read in place of the one initial state
+    state = 64 * 128 * 4
     assert rec["passes"]["output"]["algorithmic_bytes_per_launch"] == \
-        bench.chunk_algorithmic(1, 65536, 16, 64, 128, 32, state_in=True)[0]
+        bench.chunk_algorithmic(1, 65536, 16, 64, 128, 64, state_in=True)[0] - 16 * state + 16 * 16 * state
+    assert rec["call_algorithmic_bytes"] == bench.chunk_algorithmic(1, 65536, 16, 64, 128, 64, state_in=True)[0]
     sha = hashlib.sha256(open(bench.KERNEL_SRC, "rb").read()).hexdigest()
     got = bench.kernel_traffic("output")
     assert got == (rec["passes"]["output"]["hbm_bytes_per_launch"]
