@@ -160,7 +160,7 @@ size_t rodimus_ddts_chunk_fwd_ex_workspace_bytes(int B, int T, int H, int dk, in
  *   Limit: the plan's workspace (rodimus_ddts_chunk_fwd_plan) must be at most
  *   RODIMUS_STATIC_SCRATCH_BYTES, else RODIMUS_ERR_WORKSPACE is returned with
  *   nothing enqueued (e.g. B * H = 16 heads of 64 x 128 split into 16
- *   segments need 8.5 MB).
+ *   segments, 30 transfer pieces, need 15.9 MB).
  *   The buffer is one per GPU, held by every GPU the library runs on until
  *   the process ends, and shared by every call on that GPU: calls that
  *   overlap on one GPU (several streams or host threads) race on it and must
