@@ -103,6 +103,16 @@ def test_whole_head_tile_segmented(R, dev, dk):
     check_full(R, x, dev, s0=x.initial_state, label=f"whole-head dk {dk} {p}")
 
 
+def test_whole_head_tile_batched_ragged(R, dev):
+    # two sequences of 8,293 tokens x 8 heads (16 head-sequences, ragged against
+    # 64- and 32-token chunks): whole-head tiles, 15 segments of 9 chunks,
+    # transfers of half-length chunks cut in 2; initial state and S_T per (b, h)
+    x = D.make("long_prefill", B=2, T=8192 + 101, H=8)
+    p = R.chunk_fwd_plan(2, x.wl.T, 8, 64, 128)
+    assert p["dv_tile"] == 128 and p["segments"] > 1 and p["transfer_pieces"] == 2, p
+    check_full(R, x, dev, s0=x.initial_state, label=f"whole-head B2 H8 {p}")
+
+
 @pytest.mark.timeout(600)
 def test_long_prefill_full(R, dev):
     x = D.make("long_prefill")
