@@ -602,6 +602,8 @@ rodimus_status rodimus_swska_fwd(int B, int T, int H, int dk, int dv, int window
     if (!(scale >= 0.f) || scale > 3.0e38f) return RODIMUS_ERR_INVALID_ARG;   // NaN, negative, Inf
     if ((long long)B * ((T + 63) / 64) * H > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
     if ((long long)B * T > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
+    // byte offsets within a 64-key tile of v are 32-bit
+    if ((long long)64 * H * dv * 2 > (1LL << 31) - 1) return RODIMUS_ERR_INVALID_ARG;
     if (T == 0) return RODIMUS_OK;
     const void *ins[3] = {q, k, v};
     for (const void *p : ins)

@@ -306,7 +306,8 @@ rodimus_status rodimus_ddts_decode_step_fused(
  * head h and token t:
  *     o[b,t,h] = sum over t - window < s <= t of softmax_s(scale q[b,t,h] . k[b,s]) v[b,s,h]
  *
- *   B, T, H       sizes; B, H >= 1, T >= 0 (T == 0 does nothing).
+ *   B, T, H       sizes; B, H >= 1, T >= 0 (T == 0 does nothing); B * T and
+ *                 64 * H * dv * 2 below 2^31 (RODIMUS_ERR_INVALID_ARG).
  *   dk, dv        64 or 128.
  *   window        tokens each query attends to, itself included (>= 1).
  *   scale         score scale; 0 = 1 / sqrt(dk).  Negative, Inf or NaN:
