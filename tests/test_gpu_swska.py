@@ -42,6 +42,20 @@ def test_small_full(R, window):
     assert np.isfinite(o).all() and e <= 1e-2
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128, 129, 192])
+@pytest.mark.parametrize("window", [3, 64, 1000])
+def test_tile_edges(R, T, window):
+    """Sequences shorter than, equal to and just past one 64-key tile and one
+    128-query block, with windows inside a tile, equal to one, and past T
+    (H = 3: the block count is not a multiple of 8, the XCD remap is off)."""
+    x = D.make_swska(B=1, T=T, H=3)
+    o = gpu(R, x, window)
+    ro = oracle.swska_fwd(x.f32("q"), x.f32("k"), x.f32("v"), window)
+    e = oracle.rel_to_rms_error(o, ro)
+    print(f"[swska T{T} window {window}] err {e:.2e}", flush=True)
+    assert np.isfinite(o).all() and e <= 1e-2
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
 def test_widths(R, dk, dv):
     x = D.make_swska(B=1, T=200, H=3, dk=dk, dv=dv)
