@@ -36,7 +36,7 @@
 // runs only on tiles a window edge crosses.  Block ids put the heads of one
 // query block on one XCD, so the shared key tile is read from HBM once and
 // from that XCD's L2 by the other heads.
-#include "internal.h"
+#include "chunk_kernel.h"
 
 #include <math.h>
 
@@ -83,45 +83,13 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane m
-// passes the address of 4 consecutive 16-bit values (row m/4, columns
-// 4*(m%4)..+3 of a 4 x 16 block); lane i receives column i, rows 0..3.
+// The chunk kernels' device helpers: the transposing LDS read, buffer
+// resources, the packed bf16 dot product and the opaque SGPR constant.
+using chunk_detail::dot2_bf16;
+using chunk_detail::make_rsrc;
+using chunk_detail::sgpr_const;
 __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char *p) {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s *)(const_cast<unsigned char *>(p)));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
-// Buffer resource over [p, p + bytes) (raw, 32-bit data format); the
-// arguments are wave-uniform, which readfirstlane states to the compiler so
-// the descriptor stays in SGPRs.  bytes is clamped to 31 bits.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, long long bytes) {
-    if (bytes < 0) bytes = 0;
-    if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-    const unsigned long long a = (unsigned long long)p;
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-    void *base = (void *)(((unsigned long long)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, n, 0x00020000);
-}
-
-// a.lo * b.lo + a.hi * b.hi + c on packed bf16 pairs (v_dot2_f32_bf16); the
-// products are exact.
-__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float c) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b), c,
-                                          false);
-}
-
-// A constant in an SGPR, materialised by an instruction the optimiser does
-// not look through (so the dot products below keep their form).
-template <unsigned V>
-__device__ __forceinline__ unsigned sgpr_const() {
-    unsigned r;
-    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
-    return r;
+    return chunk_detail::lds_read_tr((const __bf16 *)p);
 }
 
 // Two fp32 values split into hi and lo bf16 pairs (round to nearest even);
