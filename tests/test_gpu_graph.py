@@ -128,3 +128,26 @@ def test_chunk_bwd_graph_replays(R):
         torch.cuda.synchronize()
         for n, a in ref.items():
             assert torch.equal(held[n], a), f"replay {rep}: {n} differs from the eager call"
+
+
+def test_swska_graph_replays(R):
+    """The SW-SKA entry (direct global-to-LDS loads, no scratch) captured and
+    replayed: every replay equals the eager call."""
+    dev = torch.device("cuda:0")
+    x = D.make_swska(B=2, T=777, H=4)
+    q, k, v = (x.torch(n, dev) for n in ("q", "k", "v"))
+    out = torch.empty(2, 777, 4, x.wl.dv, device=dev)
+
+    def call():
+        R.swska_fwd(q, k, v, 200, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = capture(call)
+    for rep in range(REPLAYS):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}: outputs differ from the eager call"
