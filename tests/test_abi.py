@@ -398,4 +398,6 @@ def test_swska_argument_checks():
     assert call(v=v + 2) == R.ERR_INVALID_ARG           # misaligned
     assert call(o=q) == R.ERR_INVALID_ARG               # out over q
     assert call(o=k + 1024) == R.ERR_INVALID_ARG        # out over k
+    # byte offsets within a 64-key tile of v are 32-bit: 64 * H * dv * 2 < 2^31
+    assert call(H=(1 << 31) // (64 * 128 * 2)) == R.ERR_INVALID_ARG
     assert call(T=0) == R.OK                             # nothing to do, nothing launched
