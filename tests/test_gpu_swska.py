@@ -98,3 +98,32 @@ def test_deterministic(R):
     a = gpu(R, x, 128)
     b = gpu(R, x, 128)
     assert np.array_equal(a, b)
+
+
+def _swska_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append(dict(
+            i=i, B=int(rng.integers(1, 4)), T=int(rng.choice([1, 31, 64, 127, 129, 250, 513, 700])),
+            H=int(rng.integers(1, 7)), dk=int(rng.choice([64, 128])), dv=int(rng.choice([64, 128])),
+            window=int(rng.choice([1, 2, 33, 64, 65, 200, 512, 100000])),
+            scale=float(rng.choice([0.0, 0.0, 0.05, 0.5]))))
+    return cases
+
+
+SWSKA_CASES = _swska_cases(16, 7)
+
+
+@pytest.mark.parametrize("c", SWSKA_CASES, ids=lambda c: f"{c['i']}-B{c['B']}T{c['T']}H{c['H']}-"
+                         f"{c['dk']}x{c['dv']}-w{c['window']}-s{c['scale']}")
+def test_random_shapes(R, c):
+    """Seeded random shapes, windows and scales (one fixed seed: every run
+    checks the same cases)."""
+    x = D.make_swska(B=c["B"], T=c["T"], H=c["H"], dk=c["dk"], dv=c["dv"])
+    o = gpu(R, x, c["window"], c["scale"])
+    ro = oracle.swska_fwd(x.f32("q"), x.f32("k"), x.f32("v"), c["window"],
+                          scale=c["scale"] if c["scale"] > 0 else None)
+    e = oracle.rel_to_rms_error(o, ro)
+    print(f"[swska random {c}] err {e:.2e}", flush=True)
+    assert np.isfinite(o).all() and e <= 1e-2
