@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(128, false, dk128)
+RODIMUS_DEFINE_CHUNK(128, 0, dk128)
 }  // namespace rodimus

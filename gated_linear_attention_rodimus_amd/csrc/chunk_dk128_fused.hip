@@ -4,5 +4,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(128, true, dk128_fu)
+RODIMUS_DEFINE_CHUNK(128, 1, dk128_fu)
 }  // namespace rodimus

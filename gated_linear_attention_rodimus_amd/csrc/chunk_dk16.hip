@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(16, false, dk16)
+RODIMUS_DEFINE_CHUNK(16, 0, dk16)
 }  // namespace rodimus

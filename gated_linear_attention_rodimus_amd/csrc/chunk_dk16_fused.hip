@@ -4,5 +4,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(16, true, dk16_fu)
+RODIMUS_DEFINE_CHUNK(16, 1, dk16_fu)
 }  // namespace rodimus

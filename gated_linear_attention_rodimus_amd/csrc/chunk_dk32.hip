@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(32, false, dk32)
+RODIMUS_DEFINE_CHUNK(32, 0, dk32)
 }  // namespace rodimus

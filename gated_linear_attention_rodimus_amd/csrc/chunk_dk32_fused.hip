@@ -4,5 +4,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(32, true, dk32_fu)
+RODIMUS_DEFINE_CHUNK(32, 1, dk32_fu)
 }  // namespace rodimus

@@ -3,5 +3,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(64, false, dk64)
+RODIMUS_DEFINE_CHUNK(64, 0, dk64)
 }  // namespace rodimus

@@ -4,5 +4,5 @@
 #include "chunk_kernel.h"
 
 namespace rodimus {
-RODIMUS_DEFINE_CHUNK(64, true, dk64_fu)
+RODIMUS_DEFINE_CHUNK(64, 1, dk64_fu)
 }  // namespace rodimus

@@ -1,0 +1,10 @@
+// chunk_dk64_fused_noconv.hip -- chunk-forward kernels for dk = 64 with the
+// fused steps that need no history rows (beta_hat from low-rank factors, the
+// feedthrough d): the fused kernels without the ShortConv, which keep no
+// convolution window, taps or extra v rows.  The kernel itself is in
+// chunk_kernel.h.
+#include "chunk_kernel.h"
+
+namespace rodimus {
+RODIMUS_DEFINE_CHUNK(64, 2, dk64_fn)
+}  // namespace rodimus

@@ -39,6 +39,10 @@ hipError_t launch_chunk_dk16_fu(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk32_fu(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk64_fu(const ChunkLaunch &, hipStream_t);
 hipError_t launch_chunk_dk128_fu(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk16_fn(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk32_fn(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk64_fn(const ChunkLaunch &, hipStream_t);
+hipError_t launch_chunk_dk128_fn(const ChunkLaunch &, hipStream_t);
 
 namespace {
 
@@ -137,13 +141,21 @@ int chunk_per_cu(int dk, int dvt, int C, bool f32_inputs, bool outputs, bool fus
     return 1;
 }
 
+// The fused steps without a ShortConv run the kernels compiled without it (no
+// window rows, taps or padding; their LDS layout is no larger and they are
+// compiled for the same shapes, so the plan made for the fused kernels holds).
 hipError_t launch_chunk(const ChunkLaunch &Lc, hipStream_t stream)
 {
+    const bool conv = Lc.fused && Lc.fu.conv_w > 1;
     switch (Lc.dk) {
-    case 16: return Lc.fused ? launch_chunk_dk16_fu(Lc, stream) : launch_chunk_dk16(Lc, stream);
-    case 32: return Lc.fused ? launch_chunk_dk32_fu(Lc, stream) : launch_chunk_dk32(Lc, stream);
-    case 64: return Lc.fused ? launch_chunk_dk64_fu(Lc, stream) : launch_chunk_dk64(Lc, stream);
-    case 128: return Lc.fused ? launch_chunk_dk128_fu(Lc, stream) : launch_chunk_dk128(Lc, stream);
+    case 16: return !Lc.fused ? launch_chunk_dk16(Lc, stream)
+                              : conv ? launch_chunk_dk16_fu(Lc, stream) : launch_chunk_dk16_fn(Lc, stream);
+    case 32: return !Lc.fused ? launch_chunk_dk32(Lc, stream)
+                              : conv ? launch_chunk_dk32_fu(Lc, stream) : launch_chunk_dk32_fn(Lc, stream);
+    case 64: return !Lc.fused ? launch_chunk_dk64(Lc, stream)
+                              : conv ? launch_chunk_dk64_fu(Lc, stream) : launch_chunk_dk64_fn(Lc, stream);
+    case 128: return !Lc.fused ? launch_chunk_dk128(Lc, stream)
+                               : conv ? launch_chunk_dk128_fu(Lc, stream) : launch_chunk_dk128_fn(Lc, stream);
     }
     return hipErrorInvalidValue;
 }

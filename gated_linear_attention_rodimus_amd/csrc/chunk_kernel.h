@@ -272,12 +272,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
 // Compile-time shape of one instantiation, and its LDS layout (bytes).  The
 // segment-transfer mode (OUT_ false) keeps no Qt planes, score tiles or
 // output tile.
-template <int DK, int DVT, int C, int NS_, bool OUT_ = true, bool FU_ = false>
+template <int DK, int DVT, int C, int NS_, bool OUT_ = true, int FU_ = 0>
 struct Cfg {
     static constexpr int NS = NS_;
     static constexpr bool OUT = OUT_;
-    static constexpr bool FU = FU_;                           // fused steps compiled in
-    static constexpr int HALO = FU_ ? 3 : 0;                  // ShortConv history rows (4 taps)
+    static constexpr bool FU = FU_ != 0;                      // fused steps compiled in
+    static constexpr bool CONV = FU_ == 1;                    // ... with the ShortConv (2: without)
+    static constexpr int HALO = CONV ? 3 : 0;                 // ShortConv history rows (4 taps)
     static constexpr int NP = 4;                              // producer waves
     static constexpr int NJ = DVT / 16;                       // consumer waves
     static constexpr int NW = NP + NJ;
@@ -303,10 +304,10 @@ struct Cfg {
     static constexpr size_t tot_off = a_off + (OUT ? (size_t)NA * NS * 64 * 4 * 2 : 0);
     static constexpr size_t mid_off = tot_off + (size_t)NG * DK * 4;
     // per consumer wave: raw v rows of one chunk (with the convolution's
-    // history rows and one row of padding in FU kernels), [SV][16] bf16, then
+    // history rows and one row of padding in ShortConv kernels), [SV][16] bf16, then
     // beta_hat, [C][16]
     static constexpr size_t stg_off = mid_off + (size_t)DK * 4;
-    static constexpr int SV = C + (FU_ ? HALO + 1 : 0);
+    static constexpr int SV = C + (CONV ? HALO + 1 : 0);
     static constexpr size_t stg_wave = (size_t)(SV + C) * 16 * 2;
     // output tile of one chunk, [C][OS] fp32 (row stride DVT + 16 floats: the
     // four row groups of an MFMA C-layout write land in distinct banks)
@@ -320,13 +321,13 @@ struct Cfg {
     // one otherwise, and always one for the 12-wave 128-column tile
     static constexpr int per_cu =
         ((C <= 32 || (!OUT && (DK < 64 || DVT < 64))) && NS == 2 && 2 * bytes <= 160 * 1024 &&
-         DK <= 64 && !FU_ && (NW <= 8 || (!OUT && C <= 32))) ? 2 : 1;
+         DK <= 64 && !FU && (NW <= 8 || (!OUT && C <= 32))) ? 2 : 1;
     static constexpr int waves_per_eu = (per_cu * NW + 3) / 4;
     static_assert(NG >= 1 && TPG * NG == C, "token groups");
     static_assert(C % 16 == 0 && DK % 16 == 0 && DVT % 16 == 0, "tile multiples");
 };
 
-template <int DK, int DVT, int C, typename TIn, bool OUT, bool FU>
+template <int DK, int DVT, int C, typename TIn, bool OUT, int FU>
 __global__ __launch_bounds__((Cfg<DK, DVT, C, 2>::NT),
                              (Cfg<DK, DVT, C, std::is_same<TIn, float>::value ? 3 : 2, OUT, FU>::waves_per_eu))
 void chunk_fwd_kernel(Args a)
@@ -383,7 +384,7 @@ void chunk_fwd_kernel(Args a)
     // q, k, v of FU kernels: [B][T + conv_w - 1][H][D], the convolution's
     // history rows first; row X of a chunk's window is raw token t0 + X - HALO,
     // stored at row t0 + X - HALO + conv_w - 1 (rows before 0 read as zero)
-    const int conv_w = FU ? a.conv_w : 1;
+    const int conv_w = L::CONV ? a.conv_w : 1;
     const long long Tx = T + conv_w - 1;
     const long long head0x = (long long)b * Tx * H + h;
     const long long xshift = (long long)conv_w - 1;            // stored row - raw token
@@ -680,7 +681,7 @@ void chunk_fwd_kernel(Args a)
     constexpr int LV = C >= 32 ? C / 32 : 1;             // 16-byte loads per tensor
     // FU: v window rows X = 0 .. C + HALO - 1 (raw token t0 + X - HALO)
     constexpr int LVX = FU ? (C + HALO + 31) / 32 : LV;
-    constexpr int NX = FU && !kStage ? 4 : 1;            // fp32 FU: a load per tap
+    constexpr int NX = L::CONV && !kStage ? 4 : 1;       // fp32 ShortConv: a load per tap
     u32x4 rvw[LVX], rbw[LV];
     Raw rv[KSC][8][NX], rb[KSC][8];
     __bf16 *stg = (__bf16 *)(smem + L::stg_off + (size_t)(producer ? 0 : cw) * L::stg_wave);
@@ -708,6 +709,34 @@ void chunk_fwd_kernel(Args a)
             for (int n = 0; n < NS; ++n) wB[n] = pack8(w4[0][n], w4[1][n], w4[2][n], w4[3][n]);
         }
     }
+    // FU: the chunk's u rows (issued ahead of the output stores, so that the
+    // wait for them in phase 2 does not also wait for those stores)
+    auto load_u = [&](int ch) {
+        if constexpr (FU) {
+            const long long t0 = (long long)ch * C;
+            const long long ru_row = H * (long long)a.rank;
+            const __amdgpu_buffer_rsrc_t Ru = make_rsrc(
+                (const Raw *)a.u + ((long long)b * T * H + h) * a.rank + t0 * ru_row,
+                ((T - t0) * H - h) * (long long)a.rank * esz);
+#pragma unroll
+            for (int t16 = 0; t16 < NU; ++t16)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const unsigned o = (unsigned)(((16 * t16 + lc) * ru_row + 16 * half + 4 * lg) * esz);
+                    if constexpr (NS == 2) {
+                        if (half == 0 || a.rank > 16)
+                            ru[t16][half] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Ru, o, 0, 0));
+                        else
+                            ru[t16][half] = uint2{0u, 0u};
+                    } else {
+                        if (half == 0 || a.rank > 16)
+                            ru[t16][half] = __builtin_amdgcn_raw_buffer_load_b128(Ru, o, 0, 0);
+                        else
+                            ru[t16][half] = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+        }
+    };
     auto load_v = [&](int ch, bool valid) {
         const long long t0 = (long long)ch * C;
         const long long base = t0 * row_v;
@@ -716,29 +745,6 @@ void chunk_fwd_kernel(Args a)
         if constexpr (FU) {
             const long long lx = valid ? ((Tx - t0) * H - h) * dv * esz - (long long)jcol * esz : 0;
             const __amdgpu_buffer_rsrc_t Rv = make_rsrc(gv + base, lx);
-            if (lowrank) {
-                const long long ru_row = H * (long long)a.rank;
-                const __amdgpu_buffer_rsrc_t Ru = make_rsrc(
-                    (const Raw *)a.u + ((long long)b * T * H + h) * a.rank + t0 * ru_row,
-                    valid ? ((T - t0) * H - h) * (long long)a.rank * esz : 0);
-#pragma unroll
-                for (int t16 = 0; t16 < NU; ++t16)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const unsigned o = (unsigned)(((16 * t16 + lc) * ru_row + 16 * half + 4 * lg) * esz);
-                        if constexpr (NS == 2) {
-                            if (half == 0 || a.rank > 16)
-                                ru[t16][half] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Ru, o, 0, 0));
-                            else
-                                ru[t16][half] = uint2{0u, 0u};
-                        } else {
-                            if (half == 0 || a.rank > 16)
-                                ru[t16][half] = __builtin_amdgcn_raw_buffer_load_b128(Ru, o, 0, 0);
-                            else
-                                ru[t16][half] = u32x4{0u, 0u, 0u, 0u};
-                        }
-                    }
-            }
             if constexpr (kStage) {
 #pragma unroll
                 for (int j = 0; j < LVX; ++j) {
@@ -804,7 +810,10 @@ void chunk_fwd_kernel(Args a)
                 }
         }
     };
-    if (c_begin < c_end) load_v(c_begin, true);
+    if (c_begin < c_end) {
+        if (lowrank) load_u(c_begin);
+        load_v(c_begin, true);
+    }
 
     // the block's output tile of chunk ch (staged in LDS by all consumer waves)
     // to HBM: each wave stores C / NJ whole rows of DVT floats with 16-byte
@@ -838,6 +847,41 @@ void chunk_fwd_kernel(Args a)
                 tv[j] = j < conv_w ? a.cv[((size_t)h * a.dv + jcol + lc) * conv_w + j] : 0.f;
         if (a.dfeed) dcol = a.dfeed[(size_t)h * a.dv + jcol + lc];
     }
+    // FU: low-rank beta_hat of the chunk whose u rows are in ru, formed in
+    // phase 2 of the iteration that loads them (where the consumers would
+    // otherwise wait at the barrier) and used in the next phase 1: z = u w,
+    // one MFMA per 16-token tile (C-layout: token row 4 lg + e, column lc),
+    // all tiles issued before the first sigmoid
+    float blr[FU ? 2 * KSC : 1][4];
+    auto lowrank_beta = [&]() {
+        f32x4 z[2 * KSC];
+#pragma unroll
+        for (int t16 = 0; t16 < 2 * KSC; ++t16) {
+            z[t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t16 < NU) {
+                bf16x8 uA[NS];
+                if constexpr (NS == 2) {
+                    uA[0] = pack8(ru[t16][0].x, ru[t16][0].y, ru[t16][1].x, ru[t16][1].y);
+                    z[t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uA[0], wB[0], z[t16], 0, 0, 0);
+                } else {
+                    unsigned s4[4][NS];
+                    const u32x4 lo = ru[t16][0], hi2 = ru[t16][1];
+                    split_pair<NS>(__uint_as_float(lo[0]), __uint_as_float(lo[1]), s4[0]);
+                    split_pair<NS>(__uint_as_float(lo[2]), __uint_as_float(lo[3]), s4[1]);
+                    split_pair<NS>(__uint_as_float(hi2[0]), __uint_as_float(hi2[1]), s4[2]);
+                    split_pair<NS>(__uint_as_float(hi2[2]), __uint_as_float(hi2[3]), s4[3]);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) uA[n] = pack8(s4[0][n], s4[1][n], s4[2][n], s4[3][n]);
+                    z[t16] = mma_split<NS>(uA, wB, z[t16]);
+                }
+            }
+        }
+#pragma unroll
+        for (int t16 = 0; t16 < 2 * KSC; ++t16)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                blr[t16][e] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * z[t16][e]));
+    };
 
     for (int it = c_begin; it <= c_end; ++it) {
         const bool cwork = it > c_begin;
@@ -932,36 +976,17 @@ void chunk_fwd_kernel(Args a)
                         }
                     }
                     if (lowrank) {
-                        // z = u w for the 16 tokens of tile 2p + hh (C-layout:
-                        // rows 4 lg + e, column lc), then the sigmoid
-                        const int t16 = 2 * p + hh;
-                        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        if (live) {
-                            bf16x8 uA[NS];
-                            if constexpr (NS == 2) {
-                                uA[0] = pack8(ru[t16][0].x, ru[t16][0].y, ru[t16][1].x, ru[t16][1].y);
-                                uA[1] = pack8(0u, 0u, 0u, 0u);
-                                z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uA[0], wB[0], z, 0, 0, 0);
-                            } else {
-                                unsigned s4[4][NS];
-                                const u32x4 lo = ru[t16][0], hi2 = ru[t16][1];
-                                split_pair<NS>(__uint_as_float(lo[0]), __uint_as_float(lo[1]), s4[0]);
-                                split_pair<NS>(__uint_as_float(lo[2]), __uint_as_float(lo[3]), s4[1]);
-                                split_pair<NS>(__uint_as_float(hi2[0]), __uint_as_float(hi2[1]), s4[2]);
-                                split_pair<NS>(__uint_as_float(hi2[2]), __uint_as_float(hi2[3]), s4[3]);
+                        // tile 2p + hh of this chunk's beta_hat, formed last phase 2
 #pragma unroll
-                                for (int n = 0; n < NS; ++n) uA[n] = pack8(s4[0][n], s4[1][n], s4[2][n], s4[3][n]);
-                                z = mma_split<NS>(uA, wB, z);
-                            }
-                        }
+                        for (int e = 0; e < 4; ++e) bb[4 * hh + e] = blr[2 * p + hh][e];
+                    }
+                    // tokens past the sequence end stay inert (without the
+                    // convolution their v rows already read as zero)
+                    if constexpr (L::CONV) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            bb[4 * hh + e] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * z[e]));
+                            if (tok0 + tb + e >= T) vv[4 * hh + e] = 0.f;
                     }
-                    // tokens past the sequence end stay inert
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (tok0 + tb + e >= T) vv[4 * hh + e] = 0.f;
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) vf[p][e] = vv[e];
@@ -1015,6 +1040,7 @@ void chunk_fwd_kernel(Args a)
           }
             // outputs staged last iteration (issued after the wait for this
             // chunk's v loads, so that wait does not include these stores)
+            if (lowrank && it < c_end) load_u(it);
             if (outputs && it - 2 >= c_begin) store_tile(it - 2);
             if (it < c_end) load_v(it, true);               // next chunk's v, beta_hat
 
@@ -1115,6 +1141,10 @@ void chunk_fwd_kernel(Args a)
                         mma_split_n<NS, NU - 2>(A + 2, Bv + 2, acc + 2);
                     }
                 }
+                // FU: the loaded chunk's beta_hat while these products run
+                if constexpr (FU) {
+                    if (lowrank && it < c_end) lowrank_beta();
+                }
                 // FU: feedthrough o += d * v (C-layout rows 4 lg + r of token
                 // tile U are elements 4 (U & 1) + r of k-step U / 2)
                 if constexpr (FU) {
@@ -1135,6 +1165,11 @@ void chunk_fwd_kernel(Args a)
                         sOut[(U * 16 + 4 * lg + r) * L::OS + cw * 16 + lc] = acc[U][r];
             }
         }
+        if constexpr (FU) {
+            // the same where no outputs were formed this iteration (the first,
+            // or the transfer mode)
+            if (lowrank && it < c_end && !(cwork && outputs)) lowrank_beta();
+        }
         __syncthreads();                                   // barrier B
     }
 
@@ -1151,7 +1186,7 @@ void chunk_fwd_kernel(Args a)
     }
 }
 
-template <int DK, int DVT, int C, typename TIn, bool OUT, bool FU>
+template <int DK, int DVT, int C, typename TIn, bool OUT, int FU>
 hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
@@ -1191,14 +1226,14 @@ hipError_t launch_mode(const ChunkLaunch &Lc, hipStream_t stream)
 // 128-column tile (a whole head of dv = 128: 4 producer and 8 consumer waves,
 // the gates' preparation done once per head) is compiled for bf16 inputs
 // without the fused steps, dk <= 64 and chunks of 32 or 64 tokens.
-template <int DK, int DVT, int C, int NS, bool FU>
+template <int DK, int DVT, int C, int NS, int FU>
 constexpr bool compiled_shape()
 {
     return Cfg<DK, DVT, C, NS, true, FU>::bytes <= 160 * 1024 && !(DK == 128 && C == 64) &&
            !(FU && NS == 3 && C > 16) && (DVT < 128 || (NS == 2 && !FU && DK <= 64 && C >= 32));
 }
 
-template <int DK, int DVT, int C, typename TIn, bool FU>
+template <int DK, int DVT, int C, typename TIn, int FU>
 hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
 {
     constexpr int NS = std::is_same<TIn, float>::value ? 3 : 2;
@@ -1210,8 +1245,9 @@ hipError_t launch_t(const ChunkLaunch &Lc, hipStream_t stream)
     }
 }
 
-// Instantiates every (DVT, C) tile shape for one dk, with or without the
-// fused steps (XF), and defines its size queries and launcher.
+// Instantiates every (DVT, C) tile shape for one dk, without the fused steps
+// (XF 0), with all of them (1) or with those other than the ShortConv (2), and
+// defines its size queries and launcher.
 #define RODIMUS_CHUNK_CASE_LDS(XK, XV, XC, XF)                                        \
     if (dvt == XV && C == XC)                                                         \
         return f32 ? (chunk_detail::compiled_shape<XK, XV, XC, 3, XF>()               \

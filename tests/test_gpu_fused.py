@@ -142,6 +142,36 @@ def test_all_steps_off_matches_plain_forward(R):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# The fused steps without a ShortConv (u, w and d, q, k, v without history
+# rows) run kernels compiled without the convolution; these cases cover them
+# over the shapes, dtypes and plans the cases above cover with it.
+NOCONV = [
+    ("ragged rank16", "layer130m", dict(B=2, T=333, H=3), 16, True, 0, 0),
+    ("ragged rank32", "layer130m", dict(B=2, T=333, H=3), 32, True, 0, 0),
+    ("dk16 dv16", "layer130m", dict(B=1, T=150, H=2, dk=16, dv=16), 16, False, 0, 0),
+    ("dk32 dv64", "layer130m", dict(B=1, T=150, H=2, dk=32, dv=64), 16, False, 0, 0),
+    ("dk128 dv128", "layer130m", dict(B=1, T=150, H=2, dk=128, dv=128), 16, True, 0, 0),
+    ("dk64 dv32", "layer130m", dict(B=1, T=150, H=2, dk=64, dv=32), 16, False, 0, 0),
+    ("fp32", "tiny", dict(T=77, H=2, dk=32, dv=16), 16, True, 0, 0),
+    ("segmented long prefill slice", "long_prefill", dict(T=8192 + 5, H=4), 16, True, 0, 0),
+    ("chunk 16 segments 3", "layer130m", dict(B=1, T=700, H=2), 16, False, 16, 3),
+    ("chunk 32 segments 5", "layer130m", dict(B=1, T=700, H=2), 16, False, 32, 5),
+    ("chunk 64 segments 2", "layer130m", dict(B=1, T=700, H=2), 16, True, 64, 2),
+]
+
+
+@pytest.mark.parametrize("label,wl,shape,rank,with_s0,chunk,segments", NOCONV,
+                         ids=[c[0].replace(" ", "_") for c in NOCONV])
+def test_steps_without_conv(R, label, wl, shape, rank, with_s0, chunk, segments):
+    f = D.make_fused(wl, conv_width=1, rank=rank, **shape)
+    s0 = None
+    if with_s0:
+        b = f.base.wl
+        rng = np.random.default_rng(len(label))
+        s0 = (0.1 * rng.standard_normal((b.B, b.H, b.dk, b.dv))).astype(np.float32)
+    check(R, f, f"no conv: {label}", use_conv=False, s0=s0, chunk=chunk, segments=segments)
+
+
 def test_split_sequence_carry_over(R):
     """Two calls over halves, the second fed the last W - 1 raw rows of the
     first as its history and the first's final state, equal one call."""
