@@ -172,6 +172,49 @@ def test_steps_without_conv(R, label, wl, shape, rank, with_s0, chunk, segments)
     check(R, f, f"no conv: {label}", use_conv=False, s0=s0, chunk=chunk, segments=segments)
 
 
+def draw_fused_cases(n, seed):
+    """Seeded random shapes of the fused forward: widths, dtype, chunk and
+    segment counts asked for, the ShortConv width (1: the kernels without it),
+    which of u w and d are on, the rank and the gate mean."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append(dict(
+            i=i, B=int(rng.integers(1, 3)), T=int(rng.choice([1, 5, 63, 64, 65, 129, 300])),
+            H=int(rng.integers(1, 4)), dk=int(rng.choice([16, 32, 64, 128])),
+            dv=int(rng.choice([16, 32, 64, 128])),
+            dtype="f32" if rng.random() < 0.25 else "bf16",
+            chunk=int(rng.choice([0, 16, 32, 64])), segments=int(rng.choice([0, 0, 1, 2, 5])),
+            W=int(rng.choice([1, 1, 2, 3, 4])), use_u=bool(rng.random() < 0.7),
+            use_d=bool(rng.random() < 0.5), rank=int(rng.choice([16, 32])),
+            s0=bool(rng.random() < 0.5), g_mean=float(rng.choice([0.0, 1.0, 2.0]))))
+    return cases
+
+
+FUSED_CASES = draw_fused_cases(20, 77)
+
+
+def fused_case_id(c):
+    return (f"{c['i']}-B{c['B']}T{c['T']}H{c['H']}-{c['dk']}x{c['dv']}-{c['dtype']}"
+            f"-c{c['chunk']}s{c['segments']}-W{c['W']}{'-u' + str(c['rank']) if c['use_u'] else ''}"
+            f"{'-d' if c['use_d'] else ''}{'-s0' if c['s0'] else ''}")
+
+
+@pytest.mark.parametrize("c", FUSED_CASES, ids=fused_case_id)
+def test_random_shapes(R, c):
+    """Both fused kernel families (with the ShortConv when W > 1, without it
+    otherwise) on seeded random shapes, dtypes and plans."""
+    print(f"[fused random {c}]", flush=True)
+    f = D.make_fused("layer130m", conv_width=c["W"], rank=c["rank"], B=c["B"], T=c["T"], H=c["H"],
+                     dk=c["dk"], dv=c["dv"], dtype=c["dtype"], g_mean=c["g_mean"])
+    s0 = None
+    if c["s0"]:
+        rng = np.random.default_rng(1000 + c["i"])
+        s0 = (0.1 * rng.standard_normal((c["B"], c["H"], c["dk"], c["dv"]))).astype(np.float32)
+    check(R, f, f"random {c['i']}", use_u=c["use_u"], use_d=c["use_d"], use_conv=c["W"] > 1,
+          s0=s0, chunk=c["chunk"], segments=c["segments"])
+
+
 def test_split_sequence_carry_over(R):
     """Two calls over halves, the second fed the last W - 1 raw rows of the
     first as its history and the first's final state, equal one call."""
