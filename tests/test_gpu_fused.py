@@ -313,3 +313,29 @@ def test_decode_fused_one_step(R, use_conv, use_u, use_d):
     es = oracle.rel_to_rms_error(S.cpu().numpy(), rs)
     print(f"[decode fused conv={use_conv} u={use_u} d={use_d}] out {eo:.2e} state {es:.2e}", flush=True)
     assert eo <= 1e-2 and es <= 1e-2
+
+
+@pytest.mark.parametrize("dk,dv,dtype,rank,W", [(16, 16, "bf16", 16, 4), (32, 64, "bf16", 32, 2),
+                                                (128, 128, "bf16", 16, 4), (64, 32, "f32", 32, 3),
+                                                (128, 16, "f32", 16, 4)])
+def test_decode_fused_widths(R, dk, dv, dtype, rank, W):
+    """One decode step with every fused step on, over widths, dtypes, ranks and
+    window lengths."""
+    f = D.make_fused("decode_batch", conv_width=W, rank=rank, B=12, T=1, H=3, dk=dk, dv=dv,
+                     dtype=dtype)
+    st = f.base.initial_state
+    t = {n: f.torch(n, dev()) for n in ("q", "k", "v", "g", "tau", "u", "w", "d",
+                                         "conv_q", "conv_k", "conv_v")}
+    S = torch.from_numpy(st).to(dev())
+    o = R.decode_step_fused(t["q"], t["k"], t["v"], t["g"][:, 0].contiguous(),
+                            t["tau"][:, 0].contiguous(), S, u=t["u"][:, 0].contiguous(), w=t["w"],
+                            d=t["d"], conv=(t["conv_q"], t["conv_k"], t["conv_v"]))
+    torch.cuda.synchronize()
+    ro, rs = oracle.decode_fused(f.f32("q"), f.f32("k"), f.f32("v"), f.f32("g")[:, 0],
+                                 f.f32("tau")[:, 0], st, u=f.f32("u")[:, 0], w=f.f32("w"), d=f.d,
+                                 conv=(f.conv_q, f.conv_k, f.conv_v))
+    eo = oracle.rel_to_rms_error(o.cpu().numpy(), ro)
+    es = oracle.rel_to_rms_error(S.cpu().numpy(), rs)
+    bar = BAR[dtype]
+    print(f"[decode fused dk{dk} dv{dv} {dtype} rank{rank} W{W}] out {eo:.2e} state {es:.2e}", flush=True)
+    assert eo <= bar and es <= bar
