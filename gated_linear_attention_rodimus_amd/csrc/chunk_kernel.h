@@ -621,15 +621,20 @@ void chunk_fwd_kernel(Args a)
                 }
                 const float2 mid = *(const float2 *)(sMid + c0);
                 bm0 += mid.x; bm1 += mid.y;
-                // to log2 units: b = -log2(e) * (sum of g * tau)
-                const float sh0 = (bm0 - off0) * kLog2e, sh1 = (bm1 - off1) * kLog2e;
+                // to log2 units: b = -log2(e) * (sum of g * tau).  Kt is taken
+                // relative to the reference token r: the midpoint m where it
+                // also forms the score tiles, the chunk's last token L in the
+                // transfer mode (every factor then at most 1, and the state
+                // update needs no rescaling of the product)
+                const float ref0 = outputs ? bm0 : bL0, ref1 = outputs ? bm1 : bL1;
+                const float sh0 = (ref0 - off0) * kLog2e, sh1 = (ref1 - off1) * kLog2e;
                 bm0 *= -kLog2e; bm1 *= -kLog2e;
                 bL0 *= -kLog2e; bL1 *= -kLog2e;
                 __bf16 *qb = bQ(pb), *kb = bK(pb);
 #pragma unroll
                 for (int m = 0; m < TPG; ++m) {
                     const int u = cgp * TPG + m;
-                    const float d0 = __builtin_fmaf(cum0[m], -kLog2e, sh0);      // b_u - b_m
+                    const float d0 = __builtin_fmaf(cum0[m], -kLog2e, sh0);      // b_u - b_r
                     const float d1 = __builtin_fmaf(cum1[m], -kLog2e, sh1);
                     const float la0 = log2_gate_pow(PR::lo(rg[R][m]), PR::lo(rt[R][m]));
                     const float la1 = log2_gate_pow(PR::hi(rg[R][m]), PR::hi(rt[R][m]));
@@ -650,10 +655,12 @@ void chunk_fwd_kernel(Args a)
                 if (cgp == 0) {
                     const float g0 = __builtin_amdgcn_exp2f(bL0), g1 = __builtin_amdgcn_exp2f(bL1);
                     *(float2 *)(bGam(pb) + c0) = make_float2(g0, g1);
-                    *(float2 *)(bEm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bm0),
-                                                            __builtin_amdgcn_exp2f(bm1));
-                    *(float2 *)(bGm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bL0 - bm0),
-                                                            __builtin_amdgcn_exp2f(bL1 - bm1));
+                    if (outputs) {
+                        *(float2 *)(bEm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bm0),
+                                                                __builtin_amdgcn_exp2f(bm1));
+                        *(float2 *)(bGm(pb) + c0) = make_float2(__builtin_amdgcn_exp2f(bL0 - bm0),
+                                                                __builtin_amdgcn_exp2f(bL1 - bm1));
+                    }
                     gam_acc0 *= g0;
                     gam_acc1 *= g1;
                 }
@@ -1045,15 +1052,25 @@ void chunk_fwd_kernel(Args a)
             if (it < c_end) load_v(it, true);               // next chunk's v, beta_hat
 
             // dS = diag(exp(b_L - b_m)) Kt^T V' and S = diag(exp(b_L)) S + dS;
-            // Kt^T is read with the transposing LDS read (k = tokens).  The NI
-            // row tiles are independent accumulators, issued interleaved.
+            // in the transfer mode Kt is relative to b_L, so the products
+            // accumulate straight onto diag(exp(b_L)) S.  Kt^T is read with the
+            // transposing LDS read (k = tokens).  The NI row tiles are
+            // independent accumulators, issued interleaved.
             {
                 const __bf16 *kb = bK(cb);
                 const float *gam = bGam(cb), *gmv = bGm(cb);
                 const int trow = 4 * lg + (lc >> 2), tcol = 4 * (lc & 3);
                 f32x4 acc[NI];
 #pragma unroll
-                for (int I = 0; I < NI; ++I) acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int I = 0; I < NI; ++I) {
+                    if constexpr (OUT) {
+                        acc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    } else {
+                        const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[I][r] = g0[r] * S[I][r];
+                    }
+                }
                 bf16x8 A[KSC][NI][NS], Bv[KSC][NI][NS];
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks) {
@@ -1073,10 +1090,15 @@ void chunk_fwd_kernel(Args a)
                 for (int ks = 0; ks < KSC; ++ks) mma_split_n<NS, NI>(A[ks], Bv[ks], acc);
 #pragma unroll
                 for (int I = 0; I < NI; ++I) {
-                    const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
-                    const f32x4 g1 = *(const f32x4 *)(gmv + I * 16 + 4 * lg);
+                    if constexpr (OUT) {
+                        const f32x4 g0 = *(const f32x4 *)(gam + I * 16 + 4 * lg);
+                        const f32x4 g1 = *(const f32x4 *)(gmv + I * 16 + 4 * lg);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[I][r], g0[r] * S[I][r]);
+                        for (int r = 0; r < 4; ++r) S[I][r] = __builtin_fmaf(g1[r], acc[I][r], g0[r] * S[I][r]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[I][r] = acc[I][r];
+                    }
                 }
             }
         }
