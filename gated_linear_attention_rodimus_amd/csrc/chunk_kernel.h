@@ -421,8 +421,9 @@ void chunk_fwd_kernel(Args a)
     auto score_tiles = [&](int wi, int cb) {
         constexpr int TPW = (NA + NP - 1) / NP;            // tiles per wave
         // interleave group; one tile at a time in the 12-wave 128-column tile,
-        // whose waves have 168 registers each
-        constexpr int G = L::NW > 8 ? 1 : TPW < 4 ? TPW : 4;
+        // whose waves have 168 registers each, and two for fp32 inputs (three
+        // split terms: four tiles' operands spill)
+        constexpr int G = L::NW > 8 ? 1 : NS == 3 ? (TPW < 2 ? TPW : 2) : TPW < 4 ? TPW : 4;
         const __bf16 *qb = bQ(cb), *kb = bK(cb);
 #pragma unroll
         for (int j0 = 0; j0 < TPW; j0 += G) {
@@ -688,9 +689,14 @@ void chunk_fwd_kernel(Args a)
     constexpr int LV = C >= 32 ? C / 32 : 1;             // 16-byte loads per tensor
     // FU: v window rows X = 0 .. C + HALO - 1 (raw token t0 + X - HALO)
     constexpr int LVX = FU ? (C + HALO + 31) / 32 : LV;
-    constexpr int NX = L::CONV && !kStage ? 4 : 1;       // fp32 ShortConv: a load per tap
+    constexpr int NX = L::CONV && !kStage ? 4 : 1;       // fp32 ShortConv: taps read
     u32x4 rvw[LVX], rbw[LV];
-    Raw rv[KSC][8][NX], rb[KSC][8];
+    Raw rv[KSC][8], rb[KSC][8];
+    // FU, fp32 inputs: the v rows of each 4-token run of this lane's tokens
+    // (k-step p, half hh: tokens tb .. tb + 3, tb = 32 p + 16 hh + 4 lg) with
+    // the NX - 1 rows before it; entry x is token tb + x - (NX - 1)
+    constexpr int NXW = 4 + NX - 1;
+    Raw rvx[FU ? KSC : 1][2][FU ? NXW : 1];
     __bf16 *stg = (__bf16 *)(smem + L::stg_off + (size_t)(producer ? 0 : cw) * L::stg_wave);
     __bf16 *stgb = stg + L::SV * 16;                     // staged beta_hat rows
     // FU: low-rank beta_hat.  The chunk's u rows as MFMA A operands (16-token
@@ -772,16 +778,20 @@ void chunk_fwd_kernel(Args a)
 #pragma unroll
                 for (int p = 0; p < KSC; ++p)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int u = p * 32 + (e < 4 ? e : 12 + e) + 4 * lg;
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const bool live = 32 * p + 16 * hh < C;
+                        const int tb = 32 * p + 16 * hh + 4 * lg;
 #pragma unroll
-                        for (int j = 0; j < NX; ++j) {
-                            const long long row = (long long)u - j + xshift;
+                        for (int x = 0; x < NXW; ++x) {
+                            const long long row = (long long)tb + x - (NX - 1) + xshift;
                             const unsigned o = (unsigned)((row * row_v + lc) * esz);
-                            rv[p][e][j] = u < C && (j == 0 || conv_w > 1) ? buf_load(Rv, o, Raw()) : Raw(0);
+                            rvx[p][hh][x] = live && (x >= NX - 1 || conv_w > 1) ? buf_load(Rv, o, Raw()) : Raw(0);
                         }
-                        const unsigned o = off_v + (p * 32 + (e < 4 ? e : 12 + e)) * step_v;
-                        rb[p][e] = u < C && !lowrank ? buf_load(Rb, o, Raw()) : Raw(0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const unsigned o = off_v + (p * 32 + 16 * hh + e) * step_v;
+                            rb[p][4 * hh + e] = live && !lowrank ? buf_load(Rb, o, Raw()) : Raw(0);
+                        }
                     }
             }
             return;
@@ -808,10 +818,10 @@ void chunk_fwd_kernel(Args a)
                     const int u = p * 32 + (e < 4 ? e : 12 + e);            // + 4*lg via off_v
                     if (u < C) {
                         const unsigned o = off_v + u * step_v;
-                        rv[p][e][0] = buf_load(Rv, o, Raw());
+                        rv[p][e] = buf_load(Rv, o, Raw());
                         rb[p][e] = buf_load(Rb, o, Raw());
                     } else {
-                        rv[p][e][0] = Raw(0);
+                        rv[p][e] = Raw(0);
                         rb[p][e] = Raw(0);
                     }
                 }
@@ -972,11 +982,12 @@ void chunk_fwd_kernel(Args a)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int ee = 4 * hh + e;
-                            float acc = in_to_f32(rv[p][ee][0]);
+                            float acc = in_to_f32(rvx[p][hh][e + NX - 1]);
                             if (conv_w > 1) {
                                 acc = 0.f;
 #pragma unroll
-                                for (int j = 0; j < NX; ++j) acc = __builtin_fmaf(tv[j], in_to_f32(rv[p][ee][j]), acc);
+                                for (int j = 0; j < NX; ++j)
+                                    acc = __builtin_fmaf(tv[j], in_to_f32(rvx[p][hh][e - j + NX - 1]), acc);
                             }
                             vv[ee] = acc;
                             bb[ee] = in_to_f32(rb[p][ee]);
@@ -1038,8 +1049,8 @@ void chunk_fwd_kernel(Args a)
                     unsigned w[4][NS];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e][0]),
-                                       in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1][0]), w[e]);
+                        split_pair<NS>(in_to_f32(rb[p][2 * e]) * in_to_f32(rv[p][2 * e]),
+                                       in_to_f32(rb[p][2 * e + 1]) * in_to_f32(rv[p][2 * e + 1]), w[e]);
 #pragma unroll
                     for (int n = 0; n < NS; ++n) vB[p][n] = pack8(w[0][n], w[1][n], w[2][n], w[3][n]);
                 }
@@ -1071,23 +1082,29 @@ void chunk_fwd_kernel(Args a)
                         for (int r = 0; r < 4; ++r) acc[I][r] = g0[r] * S[I][r];
                     }
                 }
-                bf16x8 A[KSC][NI][NS], Bv[KSC][NI][NS];
+                // row tiles in groups of IG (two groups for fp32 inputs at
+                // dk = 128, where all operands at once spill ~36 registers)
+                constexpr int IG = NS == 3 && NI > 4 ? NI / 2 : NI;
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) {
-                    const int s_lo = ks * 32 + trow, s_hi = s_lo + 16;
+                for (int i0 = 0; i0 < NI; i0 += IG) {
+                    bf16x8 A[KSC][IG][NS], Bv[KSC][IG][NS];
 #pragma unroll
-                    for (int I = 0; I < NI; ++I)
+                    for (int ks = 0; ks < KSC; ++ks) {
+                        const int s_lo = ks * 32 + trow, s_hi = s_lo + 16;
 #pragma unroll
-                        for (int n = 0; n < NS; ++n) {
-                            const __bf16 *base = kb + n * C * RS + I * 16 + tcol;
-                            const bf16x4 klo = lds_read_tr(base + s_lo * RS);
-                            const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
-                            A[ks][I][n] = cat(klo, khi);
-                            Bv[ks][I][n] = vB[ks][n];
-                        }
+                        for (int I = 0; I < IG; ++I)
+#pragma unroll
+                            for (int n = 0; n < NS; ++n) {
+                                const __bf16 *base = kb + n * C * RS + (i0 + I) * 16 + tcol;
+                                const bf16x4 klo = lds_read_tr(base + s_lo * RS);
+                                const bf16x4 khi = ks * 32 + 16 < C ? lds_read_tr(base + s_hi * RS) : zero4();
+                                A[ks][I][n] = cat(klo, khi);
+                                Bv[ks][I][n] = vB[ks][n];
+                            }
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KSC; ++ks) mma_split_n<NS, IG>(A[ks], Bv[ks], acc + i0);
                 }
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) mma_split_n<NS, NI>(A[ks], Bv[ks], acc);
 #pragma unroll
                 for (int I = 0; I < NI; ++I) {
                     if constexpr (OUT) {

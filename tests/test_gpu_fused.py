@@ -124,11 +124,14 @@ def test_explicit_segments_and_chunks(R):
         check(R, f, f"chunk {chunk} segments {seg}", chunk=chunk, segments=seg)
 
 
-def test_fp32_inputs(R):
-    f = D.make_fused("tiny", conv_width=4, T=77, H=2, dk=32, dv=16)
+@pytest.mark.parametrize("dk,dv", [(32, 16), (128, 32), (64, 128)])
+def test_fp32_inputs(R, dk, dv):
+    """fp32 inputs with every step on (the ShortConv windows read per lane, a
+    run of tokens and its history rows at a time), ragged T, at three widths."""
+    f = D.make_fused("tiny", conv_width=4, T=77, H=2, dk=dk, dv=dv)
     rng = np.random.default_rng(1)
-    s0 = (0.1 * rng.standard_normal((1, 2, 32, 16))).astype(np.float32)
-    check(R, f, "fp32 all steps", s0=s0)
+    s0 = (0.1 * rng.standard_normal((1, 2, dk, dv))).astype(np.float32)
+    check(R, f, f"fp32 all steps {dk}x{dv}", s0=s0)
 
 
 def test_all_steps_off_matches_plain_forward(R):
