@@ -88,3 +88,37 @@ def test_random_shape(R, c):
     errs = {n: oracle.rel_to_rms_error(g[n].cpu().numpy(), r[n]) for n in GRADS}
     bad = {n: e for n, e in errs.items() if not e <= bar}
     assert not bad, f"errors above {bar}: {bad} (all: {errs})"
+
+
+def test_random_shape_sweep(R):
+    """A wider sweep from a second seed: 160 forward shapes (outputs and final
+    states) and the backward of every other one up to T = 257, each against the
+    oracle at its bar; reports the worst error as a fraction of the bar."""
+    dev = torch.device("cuda:0")
+    tt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    worst, bad = {}, []
+    for c in draw_cases(160, 777):
+        x = D.make("layer1p6b", sub=1000 + c["i"], B=c["B"], T=c["T"], H=c["H"], dk=c["dk"],
+                   dv=c["dv"], dtype=c["dtype"], g_mean=c["g_mean"], s0_std=0.1 if c["s0"] else 0.0)
+        bar = BAR[c["dtype"]]
+        s0 = x.initial_state
+        ins = [x.f32(n) for n in NAMES]
+        t = [x.torch(n, dev) for n in NAMES]
+        o, sf = R.chunk_fwd(*t, initial_state=tt(s0), output_final_state=True, chunk=c["chunk"],
+                            segments=c["segments"])
+        torch.cuda.synchronize()
+        ro, rs = oracle.fwd(*ins, s0)
+        errs = {"out": oracle.rel_to_rms_error(o.cpu().numpy(), ro),
+                "state": oracle.rel_to_rms_error(sf.cpu().numpy(), rs)}
+        if c["i"] % 2 == 0 and c["T"] <= 257:
+            d_out = np.random.default_rng(c["i"]).standard_normal(ro.shape).astype(np.float32)
+            g = R.chunk_bwd(*t, tt(d_out), initial_state=tt(s0))
+            torch.cuda.synchronize()
+            r = oracle.bwd(*ins, d_out, s0, None)
+            errs.update({n: oracle.rel_to_rms_error(g[n].cpu().numpy(), r[n]) for n in GRADS})
+        for n, e in errs.items():
+            worst[c["dtype"]] = max(worst.get(c["dtype"], 0.0), e / bar)
+            if not e <= bar:
+                bad.append((case_id(c), n, e))
+    print(f"[sweep] worst error as a fraction of the bar: {worst}", flush=True)
+    assert not bad, bad
