@@ -342,3 +342,27 @@ def test_decode_fused_widths(R, dk, dv, dtype, rank, W):
     bar = BAR[dtype]
     print(f"[decode fused dk{dk} dv{dv} {dtype} rank{rank} W{W}] out {eo:.2e} state {es:.2e}", flush=True)
     assert eo <= bar and es <= bar
+
+
+def test_random_shape_sweep(R):
+    """A wider sweep from a second seed: 80 more shapes, dtypes, plans and step
+    mixes of the fused forward against the oracle; reports the worst error as a
+    fraction of the bar."""
+    worst, bad = {}, []
+    for c in draw_fused_cases(80, 99):
+        f = D.make_fused("layer130m", conv_width=c["W"], rank=c["rank"], B=c["B"], T=c["T"], H=c["H"],
+                         dk=c["dk"], dv=c["dv"], dtype=c["dtype"], g_mean=c["g_mean"], sub=500 + c["i"])
+        s0 = None
+        if c["s0"]:
+            rng = np.random.default_rng(2000 + c["i"])
+            s0 = (0.1 * rng.standard_normal((c["B"], c["H"], c["dk"], c["dv"]))).astype(np.float32)
+        kw = dict(use_u=c["use_u"], use_d=c["use_d"], use_conv=c["W"] > 1)
+        o, sf = run(R, f, s0=s0, chunk=c["chunk"], segments=c["segments"], **kw)
+        ro, rs = ref(f, s0=s0, **kw)
+        bar = BAR[f.base.wl.dtype]
+        for n, e in (("out", oracle.rel_to_rms_error(o, ro)), ("state", oracle.rel_to_rms_error(sf, rs))):
+            worst[c["dtype"]] = max(worst.get(c["dtype"], 0.0), e / bar)
+            if not e <= bar:
+                bad.append((fused_case_id(c), n, e))
+    print(f"[fused sweep] worst error as a fraction of the bar: {worst}", flush=True)
+    assert not bad, bad
