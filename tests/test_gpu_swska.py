@@ -127,3 +127,20 @@ def test_random_shapes(R, c):
     e = oracle.rel_to_rms_error(o, ro)
     print(f"[swska random {c}] err {e:.2e}", flush=True)
     assert np.isfinite(o).all() and e <= 1e-2
+
+
+def test_random_shape_sweep(R):
+    """A wider sweep from a second seed: 48 more shapes, windows and scales
+    against the oracle; reports the worst error as a fraction of the bar."""
+    worst, bad = 0.0, []
+    for c in _swska_cases(48, 8):
+        x = D.make_swska(sub=100 + c["i"], B=c["B"], T=c["T"], H=c["H"], dk=c["dk"], dv=c["dv"])
+        o = gpu(R, x, c["window"], c["scale"])
+        ro = oracle.swska_fwd(x.f32("q"), x.f32("k"), x.f32("v"), c["window"],
+                              scale=c["scale"] if c["scale"] > 0 else None)
+        e = oracle.rel_to_rms_error(o, ro)
+        worst = max(worst, e / 1e-2)
+        if not (np.isfinite(o).all() and e <= 1e-2):
+            bad.append((c, e))
+    print(f"[swska sweep] worst error as a fraction of the bar: {worst:.3f}", flush=True)
+    assert not bad, bad
